@@ -1,0 +1,55 @@
+// Internal declarations shared by the library's translation units.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "mxmoe.h"
+
+namespace mxmoe {
+
+// ---- errors -----------------------------------------------------------
+moe_status fail(moe_status s, const char* fmt, ...) __attribute__((format(printf, 2, 3)));
+void clear_error();
+
+#define MXMOE_HIP(call)                                                              \
+  do {                                                                               \
+    hipError_t e_ = (call);                                                          \
+    if (e_ != hipSuccess)                                                            \
+      return ::mxmoe::fail(MOE_ERR_HIP, "%s failed: %s", #call, hipGetErrorString(e_)); \
+  } while (0)
+
+#define MXMOE_TRY(expr)               \
+  do {                                \
+    moe_status s_ = (expr);           \
+    if (s_ != MOE_OK) return s_;      \
+  } while (0)
+
+// Current device must be a gfx950; cached per device id.
+moe_status check_device();
+// Compute units of the current device (cached).
+int num_cus();
+
+inline size_t align_up(size_t v, size_t a) { return (v + a - 1) / a * a; }
+
+// ---- launchers (arguments already validated) --------------------------
+moe_status launch_route(const float* logits, int T, int E, int k, int32_t* ids, float* w,
+                        hipStream_t s);
+size_t permute_ws_bytes(int T, int E, int k);
+moe_status launch_permute(const int32_t* ids, int T, int E, int k, int32_t* off, int32_t* perm_src,
+                          int32_t* dest_row, void* ws, hipStream_t s);
+size_t gemm_ws_bytes(int rows, int E);
+moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s);
+moe_status launch_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* w,
+                          int T, int k, int H, float* out, uint16_t* x_next, hipStream_t s);
+moe_status validate_gemm(const moe_gemm_args& a);
+
+// ---- layer workspace layout -------------------------------------------
+struct LayerWs {
+  size_t ids, w, off, perm_src, dest_row, inter, inter_scales, y, permute_ws, gemm_ws, total;
+};
+LayerWs layer_ws_layout(int T, int H, int I, int E, int k, int inter_dtype);
+
+}  // namespace mxmoe

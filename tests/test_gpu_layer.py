@@ -1,0 +1,199 @@
+"""The whole layer and the streamed stack on the GPU against the oracle, plus the
+invariants that need no oracle (power-of-two scales, sign flips, determinism,
+token-order permutation, pipelined == serialized)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import moe as omoe
+from workloads import gen
+from tests.gpu_util import cpu_weights, device_weights, device_x, oracle_layer, rel_err, x_as_f64
+
+pytestmark = pytest.mark.gpu
+
+mx = pytest.importorskip("mxfp4_weight_mixture_amd")
+DEV = "cuda"
+
+
+def _run(shape, li, weights=None):
+    w = weights if weights is not None else device_weights(shape)
+    layer = mx.Layer(*w, k=shape.k, layout=shape.layout)
+    x, xs = device_x(li)
+    out = layer.forward(torch.from_numpy(li.logits).to(DEV), x, xs)
+    torch.cuda.synchronize()
+    return out, layer
+
+
+def _check_layer(shape, li, tol):
+    out, layer = _run(shape, li)
+    ref, it = oracle_layer(shape, li)
+    r = {k: v.cpu().numpy() for k, v in layer.routing(shape.T).items()}
+    np.testing.assert_array_equal(r["ids"], it["ids"])
+    np.testing.assert_array_equal(r["offsets"], it["offsets"])
+    np.testing.assert_array_equal(r["perm_src"], it["perm_src"])
+    np.testing.assert_array_equal(r["dest_row"], it["dest_row"])
+    np.testing.assert_allclose(r["w"], it["w"], rtol=1e-6)
+    err = rel_err(out.cpu().numpy(), ref)
+    assert err <= tol, err
+    return err
+
+
+@pytest.mark.parametrize("layout", ["split", "interleaved"])
+@pytest.mark.parametrize("act", ["bf16", "mxfp8"])
+def test_tiny_workload(layout, act):
+    s = gen.preset("tiny", layout=layout, act=act)
+    li = gen.layer_inputs(s)
+    _check_layer(s, li, 2e-2 if act == "bf16" else 5e-2)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,layout,act", [
+    (1, 128, 64, 4, 1, "split", "bf16"),
+    (3, 256, 96, 7, 3, "interleaved", "bf16"),
+    (257, 192, 160, 16, 4, "split", "mxfp8"),
+    (64, 512, 256, 1, 1, "interleaved", "mxfp8"),
+    (600, 256, 128, 3, 2, "split", "bf16"),
+    (40, 1024, 512, 64, 8, "interleaved", "bf16"),
+])
+def test_random_shapes(T, H, I, E, k, layout, act):
+    s = gen.LayerShape(T=T, H=H, I=I, E=E, k=k, layout=layout, act=act, cfg_id=100 + T)
+    li = gen.layer_inputs(s)
+    _check_layer(s, li, 2e-2 if act == "bf16" else 5e-2)
+
+
+def test_all_tokens_to_one_expert_and_empty_experts():
+    s = gen.LayerShape(T=700, H=256, I=128, E=6, k=1, cfg_id=120)
+    li = gen.layer_inputs(s)
+    li.logits[:, 4] += 1e4          # every token -> expert 4 (three 256-row tiles); others empty
+    _check_layer(s, li, 2e-2)
+
+
+def test_zero_tokens_is_a_no_op():
+    s = gen.LayerShape(T=4, H=128, I=64, E=4, k=2, cfg_id=121)
+    layer = mx.Layer(*device_weights(s), k=2)
+    out = layer.forward(torch.zeros((0, 4), device=DEV), torch.zeros((0, 128), dtype=torch.bfloat16, device=DEV))
+    torch.cuda.synchronize()
+    assert out.shape == (0, 128)
+
+
+# ---------------------------------------------- invariants without an oracle
+
+def _inv_setup():
+    s = gen.LayerShape(T=300, H=256, I=128, E=8, k=2, cfg_id=130)
+    return s, gen.layer_inputs(s), device_weights(s)
+
+
+def test_w2_scale_plus_one_doubles_the_output_bitwise():
+    s, li, w = _inv_setup()
+    base, _ = _run(s, li, w)
+    w1p, w1s, w2p, w2s = w
+    doubled, _ = _run(s, li, (w1p, w1s, w2p, w2s + 1))
+    assert torch.equal(doubled, 2 * base)
+
+
+def test_up_row_scales_plus_one_doubles_the_output_bitwise():
+    s, li, w = _inv_setup()
+    base, _ = _run(s, li, w)
+    w1p, w1s, w2p, w2s = w
+    w1s_up = w1s.clone()
+    w1s_up[:, s.I:] += 1                 # split layout: rows [I, 2I) are "up"
+    doubled, _ = _run(s, li, (w1p, w1s_up, w2p, w2s))
+    assert torch.equal(doubled, 2 * base)
+
+
+def test_w2_sign_flip_negates_the_output():
+    """Negation is exact everywhere except inside the bf16 MFMA, whose internal
+    accumulation was measured not to be sign-symmetric (about 3 in 10^4
+    outputs differ by one fp32 ulp).  Such a difference can move FC2's bf16
+    rounding of Y by one bf16 ulp (2**-8 relative), so the bound is that."""
+    s, li, w = _inv_setup()
+    base, _ = _run(s, li, w)
+    w1p, w1s, w2p, w2s = w
+    neg, _ = _run(s, li, (w1p, w1s, w2p ^ 0x88, w2s))
+    d = (neg + base).abs()
+    assert float(d.max()) <= 2.0 ** -7 * float(base.abs().max())
+    assert float((d > 0).float().mean()) < 0.05
+
+
+def test_repeat_runs_are_bitwise_identical():
+    s, li, w = _inv_setup()
+    outs = [_run(s, li, w)[0] for _ in range(5)]
+    assert all(torch.equal(outs[0], o) for o in outs[1:])
+
+
+def test_token_order_permutation_bitwise():
+    s, li, w = _inv_setup()
+    base, _ = _run(s, li, w)
+    perm = np.random.default_rng(0).permutation(s.T)
+    lp = gen.LayerInputs(s, li.x_bf16[perm], li.logits[perm])
+    outp, _ = _run(s, lp, w)
+    assert torch.equal(outp, base[perm])
+
+
+# ------------------------------------------------------------ streamed
+
+def _pinned_blobs(s, n_blobs):
+    H, I, E = s.H, s.I, s.E
+    nbytes = mx.blob_bytes(H, I, E)
+    blobs = []
+    for b in range(n_blobs):
+        blob = torch.zeros(nbytes, dtype=torch.uint8, pin_memory=True)
+        w1p, w1s, w2p, w2s = gen.all_expert_weights(s, layer=b, device="cpu")
+        for which, t in enumerate((w1p, w1s, w2p, w2s)):
+            o = mx.blob_section_offset(H, I, E, which)
+            blob[o:o + t.numel()] = t.reshape(-1)
+        blobs.append(blob)
+    return blobs
+
+
+def _stream(s, blobs, depth, chain="rms", L=4):
+    nbytes = blobs[0].numel()
+    slots = [torch.empty(nbytes, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    logits = torch.from_numpy(np.stack([gen.router_logits(s, l) for l in range(L)])).to(DEV)
+    x = gen.activations_bf16(s).to(DEV)
+    out = torch.empty((s.T, s.H), dtype=torch.float32, device=DEV)
+    caps = torch.empty((L, s.T, s.H), dtype=torch.bfloat16, device=DEV)
+    copy = torch.cuda.Stream()
+    mx.prefill_streamed(blobs, slots, logits, x, out, T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, num_layers=L,
+                        layout=s.layout, chain=chain, depth=depth, layer_inputs=caps, copy_stream=copy)
+    torch.cuda.synchronize()
+    return out, caps, logits
+
+
+def test_streamed_pipelined_equals_serialized_and_resident():
+    s = gen.LayerShape(T=96, H=256, I=128, E=8, k=2, cfg_id=140, layers=4)
+    blobs = _pinned_blobs(s, 2)
+    out2, caps2, logits = _stream(s, blobs, depth=2)
+    out1, caps1, _ = _stream(s, blobs, depth=1)
+    assert torch.equal(out1, out2) and torch.equal(caps1, caps2)
+    assert torch.equal(caps2[0], gen.activations_bf16(s).to(DEV))
+    for L in range(4):
+        w = device_weights(s, layer=L % 2)
+        layer = mx.Layer(*w, k=s.k)
+        xn = torch.empty((s.T, s.H), dtype=torch.bfloat16, device=DEV)
+        y = layer.forward(logits[L], caps2[L], x_next=xn)
+        torch.cuda.synchronize()
+        if L < 3:
+            assert torch.equal(xn, caps2[L + 1])       # teacher-forced: same bits as the stream
+        else:
+            assert torch.equal(y, out2)
+        # and the oracle on the captured input
+        xin = omoe.activations(x_bf16=caps2[L].cpu().view(torch.int16).numpy())
+        ref = omoe.moe_layer(xin, logits[L].cpu().numpy(), s.k, cpu_weights(s, L % 2), s.layout)
+        got = y.cpu().numpy() if L == 3 else caps2[L + 1].float().cpu().numpy()
+        want = ref if L == 3 else omoe.rms_rescale(ref)
+        assert rel_err(got, want) <= 2e-2
+
+
+def test_streamed_independent_chain_and_pageable_blob_rejected():
+    s = gen.LayerShape(T=32, H=128, I=64, E=4, k=2, cfg_id=141, layers=3)
+    blobs = _pinned_blobs(s, 1)
+    out, caps, logits = _stream(s, blobs, depth=2, chain="independent", L=3)
+    x0 = gen.activations_bf16(s).to(DEV)
+    assert all(torch.equal(caps[L], x0) for L in range(3))
+    y = mx.Layer(*device_weights(s, 0), k=s.k).forward(logits[2], x0)
+    torch.cuda.synchronize()
+    assert torch.equal(y, out)
+    pageable = [torch.zeros(blobs[0].numel(), dtype=torch.uint8)]
+    with pytest.raises(mx.MoeError) as ei:
+        _stream(s, pageable, depth=2, L=3)
+    assert ei.value.status == mx.STATUS["MOE_ERR_NOT_PINNED"]
