@@ -1,0 +1,453 @@
+"""Throughput of the MXFP4 MoE layer on one MI355X.
+
+    python bench.py [--steps K] [--warmup W] [--workload NAME] [--no-cpu-baseline]
+
+A step is one pass of the layer's hot path -- route, permute, FC1 grouped
+GEMM + SwiGLU, FC2 grouped GEMM, combine -- over one batch of synthetic
+input already resident in HBM (weights, activations, logits).  The default
+workload is the Kimi-K3-shaped prefill layer (T=8192, hidden 7168, expert
+intermediate 3584, 896 experts, top-16, MXFP8 activations, Zipf-skewed
+routing, interleaved gate/up).  `--workload streamed` times the layerwise
+double-buffered prefill over 43 stacked DeepSeek-V4-Flash-shaped layers
+streamed from pinned host memory.
+
+Prints one JSON line.  Before any timing the step's output is checked
+(routing invariants, a consistent permutation, finite and repeatable
+outputs); a failed check prints no throughput.  Parity against the oracle at
+this size, in this launch configuration, is tests/test_gpu_fullsize.py.  The
+oracle runs here only in the CPU-baseline leg.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import math
+import os
+import sys
+import time
+
+import numpy as np
+import torch
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+import mxfp4_weight_mixture_amd as mx  # noqa: E402  (fails loudly if libmxmoe.so is missing)
+from workloads import gen  # noqa: E402
+
+PEAK = {  # MI355X published dense peaks
+    "hbm_GBps": 8000.0,
+    "mxfp4_TFLOPs": 10100.0,
+    "fp8_TFLOPs": 5000.0,
+    "bf16_TFLOPs": 2500.0,
+}
+METRIC = "MoE-layer prefill tokens/s + TFLOPS (% MI355X MXFP4 peak), 1 GPU"
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--workload", default="prefill896_mxfp8",
+                   choices=["prefill896_mxfp8", "prefill256", "decode", "tiny", "streamed"])
+    p.add_argument("--tokens", type=int, default=0, help="override T (decode: 1/2/8/32)")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--no-parity", action="store_true", help="skip the output checks (profiling runs)")
+    return p.parse_args()
+
+
+# ----------------------------------------------------------------- helpers
+
+class Steps:
+    """The five ABI calls of one layer, with events between them on one stream."""
+    NAMES = ["route", "permute", "fc1", "fc2", "combine"]
+
+    def __init__(self, shape, w, x, xs, logits):
+        self.s = shape
+        self.w1p, self.w1s, self.w2p, self.w2s = w
+        self.x, self.xs, self.logits = x, xs, logits
+        T, k, E, H, I = shape.T, shape.k, shape.E, shape.H, shape.I
+        dev = logits.device
+        rows = T * k
+        self.ids = torch.empty((T, k), dtype=torch.int32, device=dev)
+        self.tw = torch.empty((T, k), dtype=torch.float32, device=dev)
+        self.off = torch.empty(E + 1, dtype=torch.int32, device=dev)
+        self.ps = torch.empty(rows, dtype=torch.int32, device=dev)
+        self.dr = torch.empty(rows, dtype=torch.int32, device=dev)
+        self.act = torch.empty((rows, I), dtype=torch.bfloat16, device=dev)
+        self.y = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
+        self.out = torch.empty((T, H), dtype=torch.float32, device=dev)
+        self.pws_n = mx.lib.moe_permute_workspace_size(T, E, k)
+        self.pws = torch.empty(max(self.pws_n, 1), dtype=torch.uint8, device=dev)
+        lay = mx.LAYOUT[shape.layout]
+        self.g1 = mx.GemmArgs(a=x.data_ptr(), a_scales=xs.data_ptr() if xs is not None else None,
+                              a_gather=self.ps.data_ptr(), w_packed=self.w1p.data_ptr(),
+                              w_scales=self.w1s.data_ptr(), expert_offsets=self.off.data_ptr(),
+                              c=self.act.data_ptr(), c_scales=None, a_dtype=1 if xs is not None else 0,
+                              a_gather_div=k, a_rows=T, rows=rows, E=E, N=2 * I, K=H, epilogue=lay, c_dtype=1)
+        self.g2 = mx.GemmArgs(a=self.act.data_ptr(), a_scales=None, a_gather=None, w_packed=self.w2p.data_ptr(),
+                              w_scales=self.w2s.data_ptr(), expert_offsets=self.off.data_ptr(), c=self.y.data_ptr(),
+                              c_scales=None, a_dtype=0, a_gather_div=1, a_rows=rows, rows=rows, E=E, N=H, K=I,
+                              epilogue=0, c_dtype=1)
+        import ctypes
+        self.ctypes = ctypes
+        n = max(mx.lib.moe_grouped_gemm_workspace_size(ctypes.byref(self.g1)),
+                mx.lib.moe_grouped_gemm_workspace_size(ctypes.byref(self.g2)))
+        self.gws_n = n
+        self.gws = torch.empty(n, dtype=torch.uint8, device=dev)
+        self.ev = [torch.cuda.Event(enable_timing=True) for _ in range(6)]
+
+    def run(self, timed=False):
+        s, c = self.s, self.ctypes
+        st = c.c_void_p(torch.cuda.current_stream().cuda_stream)
+        p = lambda t: c.c_void_p(t.data_ptr())
+        ev = self.ev
+        if timed:
+            ev[0].record()
+        mx._check(mx.lib.moe_route(p(self.logits), s.T, s.E, s.k, p(self.ids), p(self.tw), st))
+        if timed:
+            ev[1].record()
+        mx._check(mx.lib.moe_permute(p(self.ids), s.T, s.E, s.k, p(self.off), p(self.ps), p(self.dr),
+                                     p(self.pws), self.pws_n, st))
+        if timed:
+            ev[2].record()
+        mx._check(mx.lib.moe_mxfp4_grouped_gemm(c.byref(self.g1), p(self.gws), self.gws_n, st))
+        if timed:
+            ev[3].record()
+        mx._check(mx.lib.moe_mxfp4_grouped_gemm(c.byref(self.g2), p(self.gws), self.gws_n, st))
+        if timed:
+            ev[4].record()
+        mx._check(mx.lib.moe_combine(p(self.y), 1, p(self.dr), p(self.tw), s.T, s.k, s.H, p(self.out), None, st))
+        if timed:
+            ev[5].record()
+
+    def split_ms(self):
+        return [self.ev[i].elapsed_time(self.ev[i + 1]) for i in range(5)]
+
+
+def hit_stats(ids, E):
+    counts = np.bincount(ids.ravel(), minlength=E)
+    return counts, int((counts > 0).sum())
+
+
+def sanity_gate(shape, steps):
+    """Oracle-free checks of one step's output before any timing (the oracle
+    comparison at this size and launch configuration is tests/test_gpu_fullsize.py):
+    routing invariants, a consistent permutation, finite outputs, and two runs
+    bitwise identical."""
+    ids = steps.ids.cpu().numpy()
+    w = steps.tw.cpu().numpy()
+    off = steps.off.cpu().numpy()
+    ps = steps.ps.cpu().numpy()
+    dr = steps.dr.cpu().numpy()
+    out1 = steps.out.clone()
+    steps.run()
+    torch.cuda.synchronize()
+    checks = {
+        "ids_in_range": bool(ids.min() >= 0 and ids.max() < shape.E),
+        "ids_distinct_per_token": bool(all(len(set(r)) == shape.k for r in ids[:: max(1, shape.T // 512)])),
+        "weights_sum_to_1": bool(np.allclose(w.sum(axis=1), 1.0, atol=1e-5)),
+        "weights_non_increasing": bool(np.all(np.diff(w, axis=1) <= 0)),
+        "offsets_match_counts": bool(np.array_equal(np.diff(off), np.bincount(ids.ravel(), minlength=shape.E))),
+        "dest_row_inverts_perm_src": bool(np.array_equal(dr[ps], np.arange(ps.size))),
+        "out_finite": bool(torch.isfinite(out1).all()),
+        "repeat_bitwise": bool(torch.equal(out1, steps.out)),
+    }
+    checks["passed"] = all(checks.values())
+    return checks
+
+
+def cpu_baseline(shape, li, ids, budget_s=25.0):
+    """The oracle timed on this host on a bounded, stratified sample of the workload.
+
+    Its cost is per expert (dequantise, two matmuls over the expert's rows) plus
+    route/permute/combine.  Route and permute run in full; a stratified sample of
+    the hit experts (evenly spaced ranks by row count, largest included) runs
+    through the oracle's expert body with its real rows; a + b*rows is fitted
+    and summed over every hit expert; the combine is timed on a token subset
+    and scaled.  Reported as tokens/s for the whole layer.
+    """
+    from oracle import moe as omoe
+    from oracle import mx as omx
+    try:
+        from threadpoolctl import threadpool_info
+        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+    except Exception:
+        threads = 1
+    t0 = time.perf_counter()
+    rid, rw = omoe.route(li.logits, shape.k)
+    offsets, perm_src, dest_row = omoe.permute(rid, shape.E)
+    t_rp = time.perf_counter() - t0
+    counts = np.diff(offsets)
+    hit = np.nonzero(counts)[0]
+    order = hit[np.argsort(counts[hit], kind="stable")]
+    if shape.act == "mxfp8":
+        xs_all = None
+    xb = li.x_bf16
+    samples = []
+    spent = 0.0
+    n_target = min(8, len(order))
+    picks = [order[int(round(q))] for q in np.linspace(0, len(order) - 1, n_target)]
+    for e in picks[::-1]:                       # largest first
+        if spent > budget_s and len(samples) >= 2:
+            break
+        lo, hi = int(offsets[e]), int(offsets[e + 1])
+        tok = perm_src[lo:hi] // shape.k
+        if shape.act == "mxfp8":
+            c, s_ = gen.quantize_mxfp8(xb[tok].float())
+            X = omoe.activations(x_codes=c.numpy(), x_scales=s_.numpy())
+        else:
+            X = omoe.activations(x_bf16=xb[tok].view(torch.int16).numpy())
+        w1p, w1s, w2p, w2s = [t.numpy() for t in gen.expert_weights(shape, int(e))]
+        t1 = time.perf_counter()
+        omoe.expert_mlp(X, omx.dequant_mxfp4(w1p, w1s), omx.dequant_mxfp4(w2p, w2s), shape.layout)
+        dt = time.perf_counter() - t1
+        spent += dt
+        samples.append((hi - lo, dt))
+    n = np.array([s[0] for s in samples], dtype=np.float64)
+    t = np.array([s[1] for s in samples], dtype=np.float64)
+    if len(samples) >= 2 and np.ptp(n) > 0:
+        b, a = np.polyfit(n, t, 1)
+        a = max(a, 0.0)
+        b = max(b, 0.0)
+    else:
+        a, b = float(t.mean()), 0.0
+    t_experts = float(len(hit) * a + b * counts[hit].sum())
+    # combine on a token subset, scaled
+    sub = min(shape.T, 256)
+    Y = np.random.default_rng(0).standard_normal((sub * shape.k, shape.H))
+    t2 = time.perf_counter()
+    omoe.combine(Y, np.arange(sub * shape.k), rw[:sub])
+    t_comb = (time.perf_counter() - t2) * shape.T / sub
+    total = t_rp + t_experts + t_comb
+    return {"value": shape.T / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
+            "sample": (f"route+permute over all {shape.T} tokens ({t_rp:.1f}s); expert body (dequantise + "
+                       f"SwiGLU MLP, float64) on {len(samples)} of {len(hit)} hit experts at evenly spaced "
+                       f"row-count ranks ({', '.join(str(int(v)) for v in n)} rows), fitted t = a + b*rows "
+                       f"(a={a:.3f}s, b={b * 1e3:.3f}ms/row) and summed over all hit experts; combine timed "
+                       f"on {sub} tokens and scaled; est. whole-layer oracle time {total:.1f}s"),
+            "host_cpus": os.cpu_count()}
+
+
+# --------------------------------------------------------------- workloads
+
+def bench_layer(args):
+    name = args.workload
+    over = {"T": args.tokens} if args.tokens else {}
+    shape = gen.preset(name, **over)
+    dev = "cuda"
+    t0 = time.time()
+    li = gen.layer_inputs(shape) if shape.act != "mxfp8" else gen.LayerInputs(
+        shape, gen.activations_bf16(shape), gen.router_logits(shape))
+    x_bf16 = li.x_bf16.to(dev)
+    if shape.act == "mxfp8":
+        x, xs = gen.quantize_mxfp8(x_bf16.float())      # input preparation, on the device
+    else:
+        x, xs = x_bf16, None
+    logits = torch.from_numpy(li.logits).to(dev)
+    w = gen.all_expert_weights(shape, 0, dev)
+    torch.cuda.synchronize()
+    log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
+
+    steps = Steps(shape, w, x, xs, logits)
+    steps.run()
+    torch.cuda.synchronize()
+    ids = steps.ids.cpu().numpy()
+    counts, n_hit = hit_stats(ids, shape.E)
+    parity = None
+    if not args.no_parity:
+        parity = sanity_gate(shape, steps)
+        log(f"[bench] checks: {parity}")
+        if not parity["passed"]:
+            print(json.dumps({"metric": METRIC, "value": None, "error": "output checks failed", "checks": parity}))
+            sys.exit(1)
+
+    for _ in range(args.warmup):
+        steps.run()
+    torch.cuda.synchronize()
+    split = np.zeros(5)
+    t_start = time.perf_counter()
+    for _ in range(args.steps):
+        steps.run(timed=True)
+        torch.cuda.synchronize()   # per step: so that the events of this step can be read
+        split += np.array(steps.split_ms())
+    t_wall = time.perf_counter() - t_start
+    split /= args.steps
+    ms = float(split.sum())
+    log(f"[bench] per step ms: " + ", ".join(f"{n} {v:.3f}" for n, v in zip(Steps.NAMES, split)))
+
+    T, H, I, k, E = shape.T, shape.H, shape.I, shape.k, shape.E
+    rows = T * k
+    flops = gen.flops(shape)
+    fc1_flops = 2.0 * rows * 2 * I * H
+    fc2_flops = 2.0 * rows * H * I
+    eb = gen.expert_bytes(shape)
+    act_bytes = T * H * (1 + 1 / 32) if shape.act == "mxfp8" else T * H * 2
+    alg_bytes = n_hit * eb + act_bytes + T * E * 4 + T * H * 4
+    fc1_w = n_hit * (2 * I * H) * 17 / 32
+    fc2_w = n_hit * (H * I) * 17 / 32
+    tflops = flops / (ms * 1e-3) / 1e12
+    fc1_ms, fc2_ms = split[2], split[3]
+    fc1_peak = PEAK["fp8_TFLOPs"] if shape.act == "mxfp8" else PEAK["bf16_TFLOPs"]
+    dom = "fc1" if fc1_ms >= fc2_ms else "fc2"
+    if name in ("decode", "tiny"):
+        # weight-streaming (HBM) bound shapes: dominant GEMM against HBM bandwidth
+        dm = fc1_ms if dom == "fc1" else fc2_ms
+        dbytes = fc1_w if dom == "fc1" else fc2_w
+        roof = {"bound": "hbm", "achieved": dbytes / (dm * 1e-3) / 1e9, "peak": PEAK["hbm_GBps"], "unit": "GB/s",
+                "traffic": None, "kernel": f"{dom} grouped GEMM", "per_launch_ms": dm,
+                "algorithmic_per_launch": dbytes}
+    else:
+        dm = fc1_ms if dom == "fc1" else fc2_ms
+        dfl = fc1_flops if dom == "fc1" else fc2_flops
+        pk = fc1_peak if dom == "fc1" else PEAK["bf16_TFLOPs"]
+        roof = {"bound": "mfma", "achieved": dfl / (dm * 1e-3) / 1e12, "peak": pk, "unit": "TFLOP/s",
+                "traffic": None, "kernel": f"{dom} grouped GEMM", "per_launch_ms": dm,
+                "algorithmic_per_launch": dfl}
+    roof["frac"] = roof["achieved"] / roof["peak"]
+    rec = {
+        "metric": METRIC,
+        "value": T / (ms * 1e-3),
+        "unit": "tokens/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": ms,
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "mxfp8xmxfp4" if shape.act == "mxfp8" else "bf16xmxfp4",
+        "data": "synthetic",
+        "config": {"workload": name, "T": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
+                   "activations": shape.act, "gate_up": shape.layout, "router_bias": shape.bias,
+                   "experts_hit": n_hit, "parallelism": "none (1 GPU)"},
+        "tflops": tflops,
+        "pct_mxfp4_peak": tflops / PEAK["mxfp4_TFLOPs"],
+        "hbm_algorithmic_GBps": alg_bytes / (ms * 1e-3) / 1e9,
+        "step_split_ms": dict(zip(Steps.NAMES, [float(v) for v in split])),
+        "wall_ms_per_step": t_wall / args.steps * 1e3,
+        "roofline": roof,
+        "checks": parity,
+    }
+    return rec, shape, li, ids
+
+
+def bench_streamed(args):
+    shape = gen.preset("streamed")
+    T, H, I, E, k, L = shape.T, shape.H, shape.I, shape.E, shape.k, shape.layers
+    dev = "cuda"
+    nbytes = mx.blob_bytes(H, I, E)
+    # distinct pinned blobs: all 43 if host memory allows, else layer L uses blob L % n
+    try:
+        import psutil
+        avail = psutil.virtual_memory().available
+    except Exception:
+        avail = 64 << 30
+    n_blobs = int(max(2, min(L, (0.5 * avail) // nbytes)))
+    t0 = time.time()
+    blobs = []
+    for b in range(n_blobs):
+        blob = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        w = gen.all_expert_weights(shape, b, dev)
+        for which, t in enumerate(w):
+            o = mx.blob_section_offset(H, I, E, which)
+            blob[o:o + t.numel()].copy_(t.reshape(-1))
+        del w
+        blobs.append(blob)
+    torch.cuda.synchronize()
+    log(f"[bench] streamed: {n_blobs} pinned blobs of {nbytes / 1e9:.3f} GB in {time.time() - t0:.1f}s")
+    slots = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
+    logits = torch.from_numpy(np.stack([gen.router_logits(shape, l) for l in range(L)])).to(dev)
+    x = gen.activations_bf16(shape).to(dev)
+    out = torch.empty((T, H), dtype=torch.float32, device=dev)
+    copy = torch.cuda.Stream()
+    ws = None
+    # measured pinned H2D peak on the same buffers (copy engine, one stream)
+    h2d = []
+    for b in range(min(2, n_blobs)):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        with torch.cuda.stream(copy):
+            e0.record()
+            slots[b % 2].copy_(blobs[b], non_blocking=True)
+            e1.record()
+        copy.synchronize()
+        h2d.append(nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
+    h2d_peak = max(h2d)
+
+    def run(depth, events=None):
+        nonlocal ws
+        ws = mx.prefill_streamed(blobs, slots, logits, x, out, T=T, H=H, I=I, E=E, k=k, num_layers=L,
+                                 layout=shape.layout, chain="rms", depth=depth, workspace=ws, events=events,
+                                 copy_stream=copy)
+
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * L)]
+    for e in ev:
+        e.record()
+    torch.cuda.synchronize()
+    for _ in range(max(1, args.warmup)):
+        run(2)
+    torch.cuda.synchronize()
+    times = []
+    for _ in range(args.steps):
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run(2, ev)
+        b.record()
+        torch.cuda.synchronize()
+        times.append(a.elapsed_time(b))
+    ms = float(np.mean(times))
+    copy_ms = [ev[4 * l].elapsed_time(ev[4 * l + 1]) for l in range(L)]
+    comp_ms = [ev[4 * l + 2].elapsed_time(ev[4 * l + 3]) for l in range(L)]
+    # serialized comparison (depth 1: copy, compute, copy, ...)
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    run(1)
+    b.record()
+    torch.cuda.synchronize()
+    ms1 = a.elapsed_time(b)
+    h2d_bytes = L * nbytes
+    achieved = h2d_bytes / (ms * 1e-3) / 1e9
+    flops = gen.flops(shape) * L
+    rec = {
+        "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "bf16xmxfp4", "data": "synthetic",
+        "config": {"workload": "streamed", "layers": L, "T": T, "hidden": H, "intermediate": I, "experts": E,
+                   "top_k": k, "distinct_host_blobs": n_blobs, "blob_GB": nbytes / 1e9,
+                   "parallelism": "none (1 GPU)"},
+        "tflops": flops / (ms * 1e-3) / 1e12,
+        "h2d_GBps": achieved, "h2d_measured_peak_GBps": h2d_peak, "h2d_frac_of_measured": achieved / h2d_peak,
+        "serialized_ms": ms1, "serialized_tokens_per_s": T / (ms1 * 1e-3),
+        "per_layer_copy_ms_mean": float(np.mean(copy_ms)), "per_layer_compute_ms_mean": float(np.mean(comp_ms)),
+        "roofline": {"bound": "h2d", "achieved": achieved, "peak": h2d_peak, "unit": "GB/s",
+                     "frac": achieved / h2d_peak, "traffic": None, "kernel": "host->device weight stream"},
+    }
+    return rec
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not sharded "
+              f"across GPUs in this build.", file=sys.stderr)
+        sys.exit(2)
+    if not torch.cuda.is_available() or not mx.device_supported():
+        print("bench.py needs an MI355X (gfx950) GPU", file=sys.stderr)
+        sys.exit(1)
+    if args.workload == "streamed":
+        rec = bench_streamed(args)
+    else:
+        rec, shape, li, ids = bench_layer(args)
+        if not args.no_cpu_baseline:
+            rec["cpu_baseline"] = cpu_baseline(shape, li, ids)
+            log(f"[bench] cpu baseline: {rec['cpu_baseline']}")
+    print(json.dumps(rec))
+
+
+if __name__ == "__main__":
+    main()
