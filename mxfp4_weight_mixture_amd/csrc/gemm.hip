@@ -365,6 +365,290 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
   }
 }
 
+// ---- main kernel: three-stage direct-to-LDS pipeline (K % 128 == 0) ----
+//
+// A stage covers 128 K elements: 4 MX blocks.  Every byte of a stage goes
+// straight from global memory into LDS with global_load_lds_dwordx4 (or
+// _dword for the scale bytes), so three stages are in flight without
+// staging registers: at iteration s the wave waits until its stage-s loads
+// have landed (stage s+1's may still be in flight), one barrier publishes
+// them and frees the buffer of stage s-1, the loads of stage s+2 are issued
+// into that buffer, then stage s is multiplied.
+//
+// LDS layout of a stage: A rows of RA bytes (128 for FP8, 256 for bf16), B
+// rows of 64 bytes (two per 128-byte line), then the four E8M0 bytes of
+// every A row (FP8 only) and of every B row.  A DMA instruction writes 64
+// lanes x 16 bytes contiguously, so the layout is chosen through each
+// lane's global address: the 16-byte slot j of a 128-byte window holds the
+// chunk j XOR (row or line mod 8).  Fragment reads of 8 consecutive rows
+// then touch 8 different slots (no bank conflicts) with no padding.
+
+template <int BM, bool FP8>
+struct Cfg2 {
+  static constexpr int WAVES_M = BM >= 128 ? 2 : 1;
+  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int WM = BM / WAVES_M;
+  static constexpr int WN = kBN / WAVES_N;
+  static constexpr int FM = WM / 32;
+  static constexpr int FN = WN / 32;
+  static constexpr int KS = 128;                    // K elements per stage
+  static constexpr int RA = FP8 ? 128 : 256;        // A bytes per row per stage
+  static constexpr int SA = RA / 16;                // 16-byte slots per A row
+  static constexpr int RB = 64;                     // B bytes per row per stage
+  static constexpr int NST = 3;
+  static constexpr int LDS_A = BM * RA;
+  static constexpr int LDS_B = kBN * RB;
+  static constexpr int LDS_AS = FP8 ? BM * 4 : 0;
+  static constexpr int LDS_BS = kBN * 4;
+  static constexpr int LDS_STAGE = LDS_A + LDS_B + LDS_AS + LDS_BS;
+  static constexpr int A_I = BM * RA / 4096;        // A DMA instructions per wave per stage
+  static constexpr int B_I = kBN * RB / 4096;       // B DMA instructions per wave per stage (4)
+  static constexpr int A_ROWS_PER_I = 1024 / RA;    // A rows one instruction fills
+  // loads a wave surely issues per stage (A, B, B scales); A scales are extra for some waves
+  static constexpr int LOADS = A_I + B_I + 1;
+};
+
+__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+}
+__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
+  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
+}
+
+template <int N>
+__device__ __forceinline__ void wait_vm() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  // s_waitcnt: vmcnt = N (bits 3:0 and 15:14), expcnt and lgkmcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
+__device__ __forceinline__ void stage_barrier() {
+  asm volatile("" ::: "memory");
+  __builtin_amdgcn_s_barrier();
+  asm volatile("" ::: "memory");
+}
+
+template <int BM, bool FP8, int EPI, int OUT>
+__global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
+  using C = Cfg2<BM, FP8>;
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::LDS_STAGE];
+
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm0 = (wave / C::WAVES_N) * C::WM;
+  const int wn0 = (wave % C::WAVES_N) * C::WN;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  const int x8 = lane & 7;         // (fragment row) mod 8, for the A swizzle
+  const int xl = (l32 >> 1) & 7;   // (fragment B line) mod 8, for the B swizzle
+
+  const int count = *p.tile_count;
+  const int units = count * p.n_tiles;
+  const int xcd = blockIdx.x % kXcds;
+  const int slot = blockIdx.x / kXcds;
+  const int slots = gridDim.x / kXcds;
+  const int per_xcd = (units + kXcds - 1) / kXcds;
+  const int u_end = min(units, (xcd + 1) * per_xcd);
+
+  const int K = p.K;
+  const int a_row_bytes = FP8 ? K : 2 * K;
+  const int kb = K / 32;
+  const int nst = K / C::KS;
+
+  for (int u = xcd * per_xcd + slot; u < u_end; u += slots) {
+    const int ti = u / p.n_tiles;
+    const int nt = u % p.n_tiles;
+    const Tile tile = p.tiles[ti];
+    const int e = tile.expert;
+    const int row0 = tile.row0;
+    const int mrows = min(BM, p.offsets[e + 1] - row0);
+    const size_t w_expert = (size_t)e * p.N;
+
+    // ---- per-lane DMA sources (stage 0; stage s adds s * bytes-per-stage) ----
+    const uint8_t* a_src[C::A_I];
+#pragma unroll
+    for (int i = 0; i < C::A_I; ++i) {
+      const int r = (wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA;
+      const int chunk = (lane % C::SA) ^ (r & 7);
+      const int grow = row0 + min(r, mrows - 1);
+      const int arow = p.a_gather ? p.a_gather[grow] / p.a_gather_div : grow;
+      a_src[i] = p.a + (size_t)arow * a_row_bytes + chunk * 16;
+    }
+    const uint8_t* b_src[C::B_I];
+#pragma unroll
+    for (int i = 0; i < C::B_I; ++i) {
+      const int line = (wave * C::B_I + i) * 8 + lane / 8;
+      const int uu = (lane & 7) ^ (line & 7);
+      const int j = line * 2 + (uu >> 2);
+      const int wr = w_row_of<C::WN>(p.layout, nt, j, p.N, p.n_out);
+      b_src[i] = p.w + (w_expert + wr) * (size_t)(K / 2) + (uu & 3) * 16;
+    }
+    const int srow = wave * 64 + lane;   // scale row this lane loads (A: if < BM)
+    const uint8_t* as_src = nullptr;
+    if (FP8 && srow < BM) {
+      const int grow = row0 + min(srow, mrows - 1);
+      const int arow = p.a_gather ? p.a_gather[grow] / p.a_gather_div : grow;
+      as_src = p.a_scales + (size_t)arow * kb;
+    }
+    const uint8_t* bs_src =
+        p.w_scales + (w_expert + w_row_of<C::WN>(p.layout, nt, srow, p.N, p.n_out)) * (size_t)kb;
+
+    auto issue = [&](int s) {
+      uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
+#pragma unroll
+      for (int i = 0; i < C::A_I; ++i)
+        lds_dma16(a_src[i] + (size_t)s * C::RA, base + (wave * C::A_I + i) * 1024);
+#pragma unroll
+      for (int i = 0; i < C::B_I; ++i)
+        lds_dma16(b_src[i] + (size_t)s * C::RB, base + C::LDS_A + (wave * C::B_I + i) * 1024);
+      if (FP8 && wave * 64 < BM) {
+        if (as_src) lds_dma4(as_src + 4 * s, base + C::LDS_A + C::LDS_B + wave * 256);
+      }
+      lds_dma4(bs_src + 4 * s, base + C::LDS_A + C::LDS_B + C::LDS_AS + wave * 256);
+    };
+
+    v16f acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    issue(0);
+    if (nst > 1) issue(1);
+
+    for (int s = 0; s < nst; ++s) {
+      if (s + 1 < nst) wait_vm<C::LOADS>();
+      else wait_vm<0>();
+      stage_barrier();
+      if (s + 2 < nst) issue(s + 2);
+      const uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
+      const uint8_t* la = base;
+      const uint8_t* lb = base + C::LDS_A;
+      const uint8_t* lsa = base + C::LDS_A + C::LDS_B;
+      const uint8_t* lsb = lsa + C::LDS_AS;
+      // four scale bytes per fragment row / column for the whole stage
+      uint32_t bsw[C::FN];
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn)
+        bsw[fn] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + fn * 32 + l32) * 4);
+      if constexpr (FP8) {
+        uint32_t asw[C::FM];
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+          asw[fm] = *reinterpret_cast<const uint32_t*>(lsa + (wm0 + fm * 32 + l32) * 4);
+#pragma unroll
+        for (int kk = 0; kk < 2; ++kk) {
+          v8i af[C::FM];
+#pragma unroll
+          for (int fm = 0; fm < C::FM; ++fm) {
+            const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
+            // K [kk*64 + 16g, +16) and [kk*64 + 32 + 16g, +16): chunks 4kk+g and 4kk+2+g
+            const v4i lo = *reinterpret_cast<const v4i*>(row + (((4 * kk + g) ^ x8) << 4));
+            const v4i hi = *reinterpret_cast<const v4i*>(row + (((4 * kk + 2 + g) ^ x8) << 4));
+            af[fm] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          }
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) {
+            const int n = wn0 + fn * 32 + l32;
+            const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xl;
+            const v4i bq = *reinterpret_cast<const v4i*>(lb + (n >> 1) * 128 + (uu << 4));
+            const v8i bf = v8i{bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
+            const int bsc = (bsw[fn] >> (8 * (2 * kk + g))) & 0xff;
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm) {
+              const int asc = (asw[fm] >> (8 * (2 * kk + g))) & 0xff;
+              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+                  af[fm], bf, acc[fm][fn], 0 /*A: fp8 e4m3*/, 4 /*B: fp4 e2m1*/, 0, asc, 0, bsc);
+            }
+          }
+        }
+      } else {
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+          // this lane's 32 weights of block 2h+g, expanded to bf16
+          v8bf bw[C::FN][4];
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) {
+            const int n = wn0 + fn * 32 + l32;
+            const int uu = ((n & 1) * 4 + 2 * h + g) ^ xl;
+            const v4i bq = *reinterpret_cast<const v4i*>(lb + (n >> 1) * 128 + (uu << 4));
+            const float sc = e8m0_to_f32((bsw[fn] >> (8 * (2 * h + g))) & 0xff);
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[d], sc, 0);
+              const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[d], sc, 1);
+              const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[d], sc, 2);
+              const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[d], sc, 3);
+              bw[fn][d] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+            }
+          }
+#pragma unroll
+          for (int s4 = 0; s4 < 4; ++s4) {
+            v8bf af[C::FM];
+#pragma unroll
+            for (int fm = 0; fm < C::FM; ++fm) {
+              const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
+              // bytes 128h + 64g + 16*s4 of the 256-byte stage row: slot 8h + 4g + s4
+              af[fm] = *reinterpret_cast<const v8bf*>(row + (((8 * h + 4 * g + s4) ^ x8) << 4));
+            }
+#pragma unroll
+            for (int fn = 0; fn < C::FN; ++fn)
+#pragma unroll
+              for (int fm = 0; fm < C::FM; ++fm)
+                acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[fm], bw[fn][s4], acc[fm][fn],
+                                                                      0, 0, 0);
+          }
+        }
+      }
+    }
+
+    // ---- epilogue: registers -> C in permuted row order ----
+    if constexpr (EPI == 0) {
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) {
+          const int n = nt * kBN + wn0 + fn * 32 + l32;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+            if (r < mrows && n < p.N) {
+              const size_t o = (size_t)(row0 + r) * p.N + n;
+              if (OUT == MOE_OUT_FP32) static_cast<float*>(p.c)[o] = acc[fm][fn][q];
+              else static_cast<uint16_t*>(p.c)[o] = (uint16_t)bf16_rne(acc[fm][fn][q]);
+            }
+          }
+        }
+    } else {
+      constexpr int HF = C::FN / 2;
+      const int i_base = nt * (kBN / 2) + (wave % C::WAVES_N) * (C::WN / 2);
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fh = 0; fh < HF; ++fh) {
+          const int i = i_base + fh * 32 + l32;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+            const float gv = acc[fm][fh][q];
+            const float uv = acc[fm][fh + HF][q];
+            const float a = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
+            if (r < mrows && i < p.n_out) {
+              const size_t o = (size_t)(row0 + r) * p.n_out + i;
+              if (OUT == MOE_OUT_FP32) static_cast<float*>(p.c)[o] = a;
+              else static_cast<uint16_t*>(p.c)[o] = (uint16_t)bf16_rne(a);
+            }
+          }
+        }
+    }
+    // every wave is done reading the stage buffers before the next unit refills them
+    stage_barrier();
+  }
+}
+
 // ---- planning: expert offsets -> per-class tile lists ------------------
 
 __device__ inline int4 wave_incl_scan4(int4 v) {
@@ -381,8 +665,10 @@ __device__ inline int4 wave_incl_scan4(int4 v) {
   return v;
 }
 
+// Full tiles have `big` rows (256 or 128) and go to class 3 or 2; an expert's
+// remainder goes to the smallest class of 32/64/128/256 rows that holds it.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E,
-                                                    Tile* __restrict__ lists, int cap,
+                                                    int big_log2, Tile* __restrict__ lists, int cap,
                                                     int32_t* __restrict__ counts) {
   __shared__ int4 wave_tot[16];
   __shared__ int4 carry;
@@ -396,9 +682,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
       start = offsets[e];
       n = offsets[e + 1] - start;
     }
-    const int full = n >> 8, rem = n & 255;
+    const int big = 1 << big_log2;
+    const int full = n >> big_log2, rem = n & (big - 1);
     const int cls = rem == 0 ? -1 : rem <= 32 ? 0 : rem <= 64 ? 1 : rem <= 128 ? 2 : 3;
-    int4 c = make_int4(cls == 0, cls == 1, cls == 2, full + (cls == 3));
+    const int full_cls = big_log2 == 8 ? 3 : 2;
+    int4 c = make_int4(cls == 0, cls == 1, (cls == 2) + (full_cls == 2 ? full : 0),
+                       (cls == 3) + (full_cls == 3 ? full : 0));
     int4 incl = wave_incl_scan4(c);
     if (lane == 63) wave_tot[wid] = incl;
     __syncthreads();
@@ -415,10 +704,12 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
     const int4 cb = carry;
     const int p0 = cb.x + incl.x - c.x, p1 = cb.y + incl.y - c.y;
     const int p2 = cb.z + incl.z - c.z, p3 = cb.w + incl.w - c.w;
-    for (int q = 0; q < full; ++q) lists[3 * cap + p3 + q] = Tile{e, start + 256 * q};
-    const int rs = start + 256 * full;
-    if (cls == 3) lists[3 * cap + p3 + full] = Tile{e, rs};
-    if (cls == 2) lists[2 * cap + p2] = Tile{e, rs};
+    // full tiles first, then the remainder, so an expert's tiles are in row order
+    const int pf = full_cls == 3 ? p3 : p2;
+    for (int q = 0; q < full; ++q) lists[full_cls * cap + pf + q] = Tile{e, start + big * q};
+    const int rs = start + big * full;
+    if (cls == 3) lists[3 * cap + p3 + (full_cls == 3 ? full : 0)] = Tile{e, rs};
+    if (cls == 2) lists[2 * cap + p2 + (full_cls == 2 ? full : 0)] = Tile{e, rs};
     if (cls == 1) lists[1 * cap + p1] = Tile{e, rs};
     if (cls == 0) lists[0 * cap + p0] = Tile{e, rs};
     __syncthreads();
@@ -435,51 +726,60 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
   }
 }
 
-int list_capacity(int rows, int E) { return rows / 32 + E + 8; }
+int list_capacity(int rows, int E) { return rows / 32 + E + 8; }  // >= rows/128 + E per class
 
-template <int BM, bool FP8, int EPI, int OUT>
+template <typename KernelT>
+int persistent_grid(KernelT kernel) {
+  int per_cu = 0;
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu < 1)
+    per_cu = 1;
+  const int grid = num_cus() * per_cu;
+  return (grid + kXcds - 1) / kXcds * kXcds;
+}
+
+template <int BM, bool FP8, int EPI, int OUT, bool DMA>
 moe_status launch_class(const Params& p, hipStream_t s) {
-  static int grid = 0;  // per-process: one device type (gfx950)
-  if (grid == 0) {
-    int per_cu = 0;
-    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, gemm_kernel<BM, FP8, EPI, OUT>,
-                                                     kThreads, 0) != hipSuccess ||
-        per_cu < 1)
-      per_cu = 1;
-    grid = num_cus() * per_cu;
-    grid = (grid + kXcds - 1) / kXcds * kXcds;
+  static int grid = 0;  // per instantiation; one device type (gfx950)
+  if constexpr (DMA) {
+    if (grid == 0) grid = persistent_grid(gemm_dma_kernel<BM, FP8, EPI, OUT>);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
+  } else {
+    if (grid == 0) grid = persistent_grid(gemm_kernel<BM, FP8, EPI, OUT>);
+    hipLaunchKernelGGL((gemm_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
   }
-  hipLaunchKernelGGL((gemm_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
   MXMOE_HIP(hipGetLastError());
   return MOE_OK;
 }
 
-template <bool FP8, int EPI, int OUT>
+template <bool FP8, int EPI, int OUT, bool DMA>
 moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* counts, hipStream_t s) {
   p.tiles = lists + 0 * cap; p.tile_count = counts + 0;
-  MXMOE_TRY((launch_class<32, FP8, EPI, OUT>(p, s)));
+  MXMOE_TRY((launch_class<32, FP8, EPI, OUT, DMA>(p, s)));
   p.tiles = lists + 1 * cap; p.tile_count = counts + 1;
-  MXMOE_TRY((launch_class<64, FP8, EPI, OUT>(p, s)));
+  MXMOE_TRY((launch_class<64, FP8, EPI, OUT, DMA>(p, s)));
   p.tiles = lists + 2 * cap; p.tile_count = counts + 2;
-  MXMOE_TRY((launch_class<128, FP8, EPI, OUT>(p, s)));
-  p.tiles = lists + 3 * cap; p.tile_count = counts + 3;
-  MXMOE_TRY((launch_class<256, FP8, EPI, OUT>(p, s)));
+  MXMOE_TRY((launch_class<128, FP8, EPI, OUT, DMA>(p, s)));
+  // the bf16 DMA kernel's full tile is 128 rows, so its class-3 list is empty
+  if constexpr (!(DMA && !FP8)) {
+    p.tiles = lists + 3 * cap; p.tile_count = counts + 3;
+    MXMOE_TRY((launch_class<256, FP8, EPI, OUT, DMA>(p, s)));
+  }
   return MOE_OK;
 }
 
-template <bool FP8, int EPI>
+template <bool FP8, int EPI, bool DMA>
 moe_status dispatch_out(const Params& p, int c_dtype, const Tile* lists, int cap,
                         const int32_t* counts, hipStream_t s) {
-  if (c_dtype == MOE_OUT_FP32) return launch_all<FP8, EPI, MOE_OUT_FP32>(p, lists, cap, counts, s);
-  if (c_dtype == MOE_OUT_BF16) return launch_all<FP8, EPI, MOE_OUT_BF16>(p, lists, cap, counts, s);
+  if (c_dtype == MOE_OUT_FP32) return launch_all<FP8, EPI, MOE_OUT_FP32, DMA>(p, lists, cap, counts, s);
+  if (c_dtype == MOE_OUT_BF16) return launch_all<FP8, EPI, MOE_OUT_BF16, DMA>(p, lists, cap, counts, s);
   return fail(MOE_ERR_NOT_IMPLEMENTED, "grouped GEMM: MXFP8 output is not provided by this build");
 }
 
-template <bool FP8>
+template <bool FP8, bool DMA>
 moe_status dispatch_epi(const Params& p, int epi, int c_dtype, const Tile* lists, int cap,
                         const int32_t* counts, hipStream_t s) {
-  if (epi == MOE_EPI_NONE) return dispatch_out<FP8, 0>(p, c_dtype, lists, cap, counts, s);
-  return dispatch_out<FP8, 1>(p, c_dtype, lists, cap, counts, s);
+  if (epi == MOE_EPI_NONE) return dispatch_out<FP8, 0, DMA>(p, c_dtype, lists, cap, counts, s);
+  return dispatch_out<FP8, 1, DMA>(p, c_dtype, lists, cap, counts, s);
 }
 
 }  // namespace
@@ -520,7 +820,12 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
   Tile* lists = static_cast<Tile*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) +
                                                align_up(kClasses * (size_t)cap * sizeof(Tile), 256));
-  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.expert_offsets, a.E, lists, cap, counts);
+  // the three-stage DMA kernels need whole 128-element K stages; other K use the register-staged ones
+  const bool dma = a.K % 128 == 0;
+  const bool fp8 = a.a_dtype == MOE_ACT_MXFP8_E4M3;
+  const int big_log2 = (dma && !fp8) ? 7 : 8;
+  hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.expert_offsets, a.E, big_log2, lists, cap,
+                     counts);
   MXMOE_HIP(hipGetLastError());
 
   Params p{};
@@ -542,9 +847,11 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
     p.n_out = a.N / 2;
     p.n_tiles = (p.n_out + kBN / 2 - 1) / (kBN / 2);
   }
-  if (a.a_dtype == MOE_ACT_MXFP8_E4M3)
-    return dispatch_epi<true>(p, a.epilogue, a.c_dtype, lists, cap, counts, s);
-  return dispatch_epi<false>(p, a.epilogue, a.c_dtype, lists, cap, counts, s);
+  if (fp8)
+    return dma ? dispatch_epi<true, true>(p, a.epilogue, a.c_dtype, lists, cap, counts, s)
+               : dispatch_epi<true, false>(p, a.epilogue, a.c_dtype, lists, cap, counts, s);
+  return dma ? dispatch_epi<false, true>(p, a.epilogue, a.c_dtype, lists, cap, counts, s)
+             : dispatch_epi<false, false>(p, a.epilogue, a.c_dtype, lists, cap, counts, s);
 }
 
 }  // namespace mxmoe
