@@ -365,23 +365,26 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
   }
 }
 
-// ---- main kernel: three-stage direct-to-LDS pipeline (K % 128 == 0) ----
+// ---- main kernel: three-stage direct-to-LDS pipeline (K % 512 == 0) ----
 //
 // A stage covers 128 K elements: 4 MX blocks.  Every byte of a stage goes
-// straight from global memory into LDS with global_load_lds_dwordx4 (or
-// _dword for the scale bytes), so three stages are in flight without
-// staging registers: at iteration s the wave waits until its stage-s loads
-// have landed (stage s+1's may still be in flight), one barrier publishes
-// them and frees the buffer of stage s-1, the loads of stage s+2 are issued
-// into that buffer, then stage s is multiplied.
+// straight from global memory into LDS with global_load_lds_dwordx4, so
+// three stages are in flight without staging registers: at iteration s the
+// wave waits until its stage-s loads have landed (stage s+1's may still be
+// in flight), one barrier publishes them and frees the buffer of stage s-1,
+// the loads of stage s+2 are issued into that buffer, then stage s is
+// multiplied.  E8M0 scales travel 16 bytes per row (four stages) at a time
+// into a double-buffered scale area: a 4-byte-per-lane load costs about as
+// much memory-pipeline time as a 16-byte one.
 //
 // LDS layout of a stage: A rows of RA bytes (128 for FP8, 256 for bf16), B
-// rows of 64 bytes (two per 128-byte line), then the four E8M0 bytes of
-// every A row (FP8 only) and of every B row.  A DMA instruction writes 64
+// rows of 64 bytes (two per 128-byte line).  A DMA instruction writes 64
 // lanes x 16 bytes contiguously, so the layout is chosen through each
-// lane's global address: the 16-byte slot j of a 128-byte window holds the
-// chunk j XOR (row or line mod 8).  Fragment reads of 8 consecutive rows
-// then touch 8 different slots (no bank conflicts) with no padding.
+// lane's global address: slot j of a 128-byte window holds chunk j XOR a
+// function of the row (or line) index, chosen so that the 16-byte fragment
+// reads of any 16 consecutive rows (one LDS cycle of a 16-lane group) hit
+// 16 different 16-byte bank groups, and any 8 consecutive rows 8 different
+// ones, with no padding.
 
 template <int BM, bool FP8>
 struct Cfg2 {
@@ -398,21 +401,27 @@ struct Cfg2 {
   static constexpr int NST = 3;
   static constexpr int LDS_A = BM * RA;
   static constexpr int LDS_B = kBN * RB;
-  static constexpr int LDS_AS = FP8 ? BM * 4 : 0;
-  static constexpr int LDS_BS = kBN * 4;
-  static constexpr int LDS_STAGE = LDS_A + LDS_B + LDS_AS + LDS_BS;
+  static constexpr int LDS_STAGE = LDS_A + LDS_B;
+  static constexpr int SG_A = FP8 ? BM * 16 : 0;    // scale group: 16 bytes (4 stages) per row
+  static constexpr int SG_B = kBN * 16;
+  static constexpr int LDS_SG = SG_A + SG_B;
+  static constexpr int LDS_TOTAL = NST * LDS_STAGE + 2 * LDS_SG;
   static constexpr int A_I = BM * RA / 4096;        // A DMA instructions per wave per stage
   static constexpr int B_I = kBN * RB / 4096;       // B DMA instructions per wave per stage (4)
   static constexpr int A_ROWS_PER_I = 1024 / RA;    // A rows one instruction fills
-  // loads a wave surely issues per stage (A, B, B scales); A scales are extra for some waves
-  static constexpr int LOADS = A_I + B_I + 1;
+  static constexpr int LOADS = A_I + B_I;           // data DMA instructions per wave per stage
+  static_assert(LDS_TOTAL <= 163840, "LDS budget");
 };
+
+// swizzle of the 16-byte slots (see above)
+template <bool FP8>
+__device__ __forceinline__ int a_swz(int r) {
+  return FP8 ? (((r >> 1) & 7) ^ ((r & 1) << 2)) : (r & 15);
+}
+__device__ __forceinline__ int b_swz(int line) { return ((line >> 1) & 3) ^ ((line & 1) << 1); }
 
 __device__ __forceinline__ void lds_dma16(const void* g, void* l) {
   __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
-}
-__device__ __forceinline__ void lds_dma4(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 4, 0, 0);
 }
 
 template <int N>
@@ -431,7 +440,7 @@ __device__ __forceinline__ void stage_barrier() {
 template <int BM, bool FP8, int EPI, int OUT>
 __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
   using C = Cfg2<BM, FP8>;
-  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::NST * C::LDS_STAGE];
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_TOTAL];
 
   const int tid = threadIdx.x;
   const int lane = tid & 63;
@@ -440,8 +449,9 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
   const int wn0 = (wave % C::WAVES_N) * C::WN;
   const int l32 = lane & 31;
   const int g = lane >> 5;
-  const int x8 = lane & 7;         // (fragment row) mod 8, for the A swizzle
-  const int xl = (l32 >> 1) & 7;   // (fragment B line) mod 8, for the B swizzle
+  // fragment rows / lines start at multiples of 16, so the swizzles depend on the lane only
+  const int xa = a_swz<FP8>(l32 & 15);
+  const int xb = b_swz((l32 >> 1) & 7);
 
   const int count = *p.tile_count;
   const int units = count * p.n_tiles;
@@ -457,8 +467,15 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
   const int nst = K / C::KS;
 
   for (int u = xcd * per_xcd + slot; u < u_end; u += slots) {
-    const int ti = u / p.n_tiles;
-    const int nt = u % p.n_tiles;
+    // units in groups of up to 4 row tiles x all n-tiles, row tile fastest, so
+    // that concurrent blocks of one XCD share both their A rows and their B tiles
+    constexpr int GM = 4;
+    const int grp = u / (GM * p.n_tiles);
+    const int first = grp * GM;
+    const int gsize = min(GM, count - first);
+    const int in = u - grp * GM * p.n_tiles;
+    const int ti = first + in % gsize;
+    const int nt = in / gsize;
     const Tile tile = p.tiles[ti];
     const int e = tile.expert;
     const int row0 = tile.row0;
@@ -470,7 +487,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < C::A_I; ++i) {
       const int r = (wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA;
-      const int chunk = (lane % C::SA) ^ (r & 7);
+      const int chunk = (lane % C::SA) ^ a_swz<FP8>(r);
       const int grow = row0 + min(r, mrows - 1);
       const int arow = p.a_gather ? p.a_gather[grow] / p.a_gather_div : grow;
       a_src[i] = p.a + (size_t)arow * a_row_bytes + chunk * 16;
@@ -479,7 +496,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
 #pragma unroll
     for (int i = 0; i < C::B_I; ++i) {
       const int line = (wave * C::B_I + i) * 8 + lane / 8;
-      const int uu = (lane & 7) ^ (line & 7);
+      const int uu = (lane & 7) ^ b_swz(line);
       const int j = line * 2 + (uu >> 2);
       const int wr = w_row_of<C::WN>(p.layout, nt, j, p.N, p.n_out);
       b_src[i] = p.w + (w_expert + wr) * (size_t)(K / 2) + (uu & 3) * 16;
@@ -493,6 +510,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
     }
     const uint8_t* bs_src =
         p.w_scales + (w_expert + w_row_of<C::WN>(p.layout, nt, srow, p.N, p.n_out)) * (size_t)kb;
+    uint8_t* const sg = lds + C::NST * C::LDS_STAGE;   // two scale groups
 
     auto issue = [&](int s) {
       uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
@@ -502,10 +520,14 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
 #pragma unroll
       for (int i = 0; i < C::B_I; ++i)
         lds_dma16(b_src[i] + (size_t)s * C::RB, base + C::LDS_A + (wave * C::B_I + i) * 1024);
+    };
+    // scale group j (stages 4j..4j+3): 16 bytes of every A and B row
+    auto issue_scales = [&](int j) {
+      uint8_t* base = sg + (j & 1) * C::LDS_SG;
       if (FP8 && wave * 64 < BM) {
-        if (as_src) lds_dma4(as_src + 4 * s, base + C::LDS_A + C::LDS_B + wave * 256);
+        if (as_src) lds_dma16(as_src + 16 * j, base + wave * 1024);
       }
-      lds_dma4(bs_src + 4 * s, base + C::LDS_A + C::LDS_B + C::LDS_AS + wave * 256);
+      lds_dma16(bs_src + 16 * j, base + C::SG_A + wave * 1024);
     };
 
     v16f acc[C::FM][C::FN];
@@ -516,29 +538,36 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
+    issue_scales(0);
     issue(0);
     if (nst > 1) issue(1);
 
     for (int s = 0; s < nst; ++s) {
+      // loads issued after stage s's: stage s+1's (and possibly a scale group); waiting
+      // for fewer outstanding than that is conservative
       if (s + 1 < nst) wait_vm<C::LOADS>();
       else wait_vm<0>();
       stage_barrier();
-      if (s + 2 < nst) issue(s + 2);
+      if (s + 2 < nst) {
+        issue(s + 2);
+        if (((s + 2) & 3) == 0) issue_scales((s + 2) >> 2);
+      }
       const uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
       const uint8_t* la = base;
       const uint8_t* lb = base + C::LDS_A;
-      const uint8_t* lsa = base + C::LDS_A + C::LDS_B;
-      const uint8_t* lsb = lsa + C::LDS_AS;
-      // four scale bytes per fragment row / column for the whole stage
+      const uint8_t* lsg = sg + ((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4;
+      const uint8_t* lsa = lsg;
+      const uint8_t* lsb = lsg + C::SG_A;
+      // four scale bytes (this stage's blocks) per fragment row / column
       uint32_t bsw[C::FN];
 #pragma unroll
       for (int fn = 0; fn < C::FN; ++fn)
-        bsw[fn] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + fn * 32 + l32) * 4);
+        bsw[fn] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + fn * 32 + l32) * 16);
       if constexpr (FP8) {
         uint32_t asw[C::FM];
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
-          asw[fm] = *reinterpret_cast<const uint32_t*>(lsa + (wm0 + fm * 32 + l32) * 4);
+          asw[fm] = *reinterpret_cast<const uint32_t*>(lsa + (wm0 + fm * 32 + l32) * 16);
 #pragma unroll
         for (int kk = 0; kk < 2; ++kk) {
           v8i af[C::FM];
@@ -546,14 +575,14 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
           for (int fm = 0; fm < C::FM; ++fm) {
             const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
             // K [kk*64 + 16g, +16) and [kk*64 + 32 + 16g, +16): chunks 4kk+g and 4kk+2+g
-            const v4i lo = *reinterpret_cast<const v4i*>(row + (((4 * kk + g) ^ x8) << 4));
-            const v4i hi = *reinterpret_cast<const v4i*>(row + (((4 * kk + 2 + g) ^ x8) << 4));
+            const v4i lo = *reinterpret_cast<const v4i*>(row + (((4 * kk + g) ^ xa) << 4));
+            const v4i hi = *reinterpret_cast<const v4i*>(row + (((4 * kk + 2 + g) ^ xa) << 4));
             af[fm] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
           }
 #pragma unroll
           for (int fn = 0; fn < C::FN; ++fn) {
             const int n = wn0 + fn * 32 + l32;
-            const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xl;
+            const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xb;
             const v4i bq = *reinterpret_cast<const v4i*>(lb + (n >> 1) * 128 + (uu << 4));
             const v8i bf = v8i{bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
             const int bsc = (bsw[fn] >> (8 * (2 * kk + g))) & 0xff;
@@ -573,7 +602,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
 #pragma unroll
           for (int fn = 0; fn < C::FN; ++fn) {
             const int n = wn0 + fn * 32 + l32;
-            const int uu = ((n & 1) * 4 + 2 * h + g) ^ xl;
+            const int uu = ((n & 1) * 4 + 2 * h + g) ^ xb;
             const v4i bq = *reinterpret_cast<const v4i*>(lb + (n >> 1) * 128 + (uu << 4));
             const float sc = e8m0_to_f32((bsw[fn] >> (8 * (2 * h + g))) & 0xff);
 #pragma unroll
@@ -592,7 +621,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
             for (int fm = 0; fm < C::FM; ++fm) {
               const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
               // bytes 128h + 64g + 16*s4 of the 256-byte stage row: slot 8h + 4g + s4
-              af[fm] = *reinterpret_cast<const v8bf*>(row + (((8 * h + 4 * g + s4) ^ x8) << 4));
+              af[fm] = *reinterpret_cast<const v8bf*>(row + (((8 * h + 4 * g + s4) ^ xa) << 4));
             }
 #pragma unroll
             for (int fn = 0; fn < C::FN; ++fn)
@@ -820,8 +849,9 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
   Tile* lists = static_cast<Tile*>(ws);
   int32_t* counts = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) +
                                                align_up(kClasses * (size_t)cap * sizeof(Tile), 256));
-  // the three-stage DMA kernels need whole 128-element K stages; other K use the register-staged ones
-  const bool dma = a.K % 128 == 0;
+  // the three-stage DMA kernels need whole groups of four 128-element K stages;
+  // other K use the register-staged kernels
+  const bool dma = a.K % 512 == 0;
   const bool fp8 = a.a_dtype == MOE_ACT_MXFP8_E4M3;
   const int big_log2 = (dma && !fp8) ? 7 : 8;
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.expert_offsets, a.E, big_log2, lists, cap,

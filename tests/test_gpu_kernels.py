@@ -101,7 +101,7 @@ def _offsets(counts):
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
 
 
-@pytest.mark.parametrize("K", [160, 384])   # 160: register-staged kernels; 384: three-stage DMA kernels
+@pytest.mark.parametrize("K", [160, 512])   # 160: register-staged kernels; 512: three-stage DMA kernels
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("counts", [[40, 0, 300], [1, 33, 64, 65, 129, 256, 257]])
 def test_gemm_one_hot_rows_return_the_dequantised_weights_bitwise(fp8, counts, K):
