@@ -47,3 +47,11 @@ def test_inputs_are_seeded():
     assert torch.equal(a.x_bf16, b.x_bf16) and np.array_equal(a.logits, b.logits)
     assert a.x_bf16.shape == (32, 128) and a.logits.shape == (32, 4)
     assert abs(float(a.x_bf16.float().std()) - 1.0) < 0.1
+
+
+def test_batched_weight_generation_matches_per_expert():
+    s = gen.LayerShape(T=4, H=256, I=96, E=11, k=2, cfg_id=78)
+    a = gen.all_expert_weights(s, layer=3, chunk=4)
+    for e in range(s.E):
+        b = gen.expert_weights(s, e, 3)
+        assert all(torch.equal(x[e], y) for x, y in zip(a, b)), e

@@ -170,25 +170,41 @@ def expert_weights(shape: LayerShape, expert: int, layer: int = 0, device="cpu")
     return w1p, w1s, w2p, w2s
 
 
-def all_expert_weights(shape: LayerShape, layer: int = 0, device="cpu", experts=None):
+def _batched_stream(keys, count: int, device) -> torch.Tensor:
+    """Words 0..count-1 of several streams at once: [len(keys)][count] (int64)."""
+    k = torch.tensor(keys, dtype=torch.int64, device=device).unsqueeze(1)
+    i = torch.arange(count, dtype=torch.int64, device=device).unsqueeze(0)
+    h = fmix32(i ^ k)
+    return fmix32((h + k) & M32)
+
+
+def all_expert_weights(shape: LayerShape, layer: int = 0, device="cpu", experts=None, chunk: int = 16):
     """Weights of all experts stacked: [E][2I][H/2], [E][2I][H/32], [E][H][I/2], [E][H][I/32].
 
-    Generated one expert at a time into preallocated tensors so that the
-    temporaries stay small even at tens of GB.
+    Byte-identical to expert_weights() per expert; generated a chunk of experts
+    per tensor op so that tens of GB take a few hundred device launches.
     """
     E = shape.E if experts is None else experts
     H, I = shape.H, shape.I
-    w1p = torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=device)
-    w1s = torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=device)
-    w2p = torch.empty((E, H, I // 2), dtype=torch.uint8, device=device)
-    w2s = torch.empty((E, H, I // 32), dtype=torch.uint8, device=device)
-    for e in range(E):
-        a, b, c, d = expert_weights(shape, e, layer, device)
-        w1p[e].copy_(a)
-        w1s[e].copy_(b)
-        w2p[e].copy_(c)
-        w2s[e].copy_(d)
-    return w1p, w1s, w2p, w2s
+    out = (torch.empty((E, 2 * I, H // 2), dtype=torch.uint8, device=device),
+           torch.empty((E, 2 * I, H // 32), dtype=torch.uint8, device=device),
+           torch.empty((E, H, I // 2), dtype=torch.uint8, device=device),
+           torch.empty((E, H, I // 32), dtype=torch.uint8, device=device))
+    kinds = ((T_W1, False), (T_S1, True), (T_W2, False), (T_S2, True))
+    for e0 in range(0, E, chunk):
+        e1 = min(E, e0 + chunk)
+        for t, (tid, is_scale) in zip(out, kinds):
+            keys = [stream_key(shape.seed, shape.cfg_id, tid, layer * shape.E + e) for e in range(e0, e1)]
+            n = t[0].numel()
+            if is_scale:
+                w = _batched_stream(keys, n, device)
+                t[e0:e1].copy_((121 + (w >> 8) % 7).to(torch.uint8).view(e1 - e0, *t.shape[1:]))
+            else:
+                w = _batched_stream(keys, (n + 3) // 4, device)
+                b = _words_to_bytes(w.reshape(-1)).view(e1 - e0, -1)[:, :n]
+                t[e0:e1].copy_(b.reshape(e1 - e0, *t.shape[1:]))
+            del w
+    return out
 
 
 # ---------------------------------------------------------------------------
