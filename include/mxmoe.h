@@ -175,8 +175,17 @@ size_t     moe_grouped_gemm_workspace_size(const moe_gemm_args* args);
  * FC2 is this call with MOE_EPI_NONE (N = H, K = I).  bf16 A runs on bf16
  * MFMA with the weights expanded exactly to bf16; MXFP8 A runs on the
  * scaled FP8 x FP4 MFMA with both E8M0 scales applied inside it.
+ * MXFP8 C (MOE_OUT_MXFP8_E4M3; SWIGLU epilogue and K % 512 == 0, else
+ * MOE_ERR_NOT_IMPLEMENTED): each row's N_out values are cut into 32-element
+ * blocks; a block with largest magnitude amax gets the E8M0 exponent X, the
+ * smallest integer with amax * 2^-X <= 448 (so no element saturates;
+ * clamped to [-127, 127]; amax == 0 gives X = -127), stored as X + 127 in
+ * c_scales, and each element v becomes the E4M3 code nearest to v * 2^-X,
+ * ties to even.  This is the intermediate of the MXFP8 x MXFP4 layer, which
+ * FC2 then reads as MXFP8 A.
  * Shape rules (MOE_ERR_SHAPE): K % 32 == 0, N % 32 == 0, N % 64 == 0 for
- * SWIGLU, N_out % 32 == 0 for MXFP8 C, rows >= 0, 1 <= E.
+ * SWIGLU, N_out % 32 == 0 for MXFP8 C, rows >= 0, 1 <= E; for K % 512 == 0
+ * also a gathered A below 4 GiB and one expert's packed weights below 4 GiB.
  */
 moe_status moe_mxfp4_grouped_gemm(const moe_gemm_args* args, void* workspace,
                                   size_t workspace_bytes, void* stream);

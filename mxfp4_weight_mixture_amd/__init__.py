@@ -158,7 +158,9 @@ def grouped_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor
                  epilogue: str = "none", out_dtype: str = "bf16", stream=None) -> torch.Tensor:
     """moe_mxfp4_grouped_gemm.  a: bf16 [a_rows][K] or uint8 E4M3 codes (with a_scales).
 
-    w_packed [E][N][K/2], w_scales [E][N][K/32].  Returns C [rows][N or N/2].
+    w_packed [E][N][K/2], w_scales [E][N][K/32].  Returns C [rows][N or N/2]
+    (fp32 or bf16), or for out_dtype "mxfp8" the pair (E4M3 codes uint8
+    [rows][N/2], E8M0 scales uint8 [rows][N/64]).
     """
     E, N, K2 = w_packed.shape
     K = 2 * K2
@@ -166,18 +168,24 @@ def grouped_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor
         rows = a_gather.numel() if a_gather is not None else a.shape[0]
     epi = {"none": 0, "split": 1, "interleaved": 2}[epilogue]
     n_out = N if epi == 0 else N // 2
-    c_dt = {"fp32": 0, "bf16": 1}[out_dtype]
-    c = torch.empty((rows, n_out), dtype=torch.float32 if c_dt == 0 else torch.bfloat16, device=a.device)
+    c_dt = {"fp32": 0, "bf16": 1, "mxfp8": 2}[out_dtype]
+    c_scales = None
+    if c_dt == 2:
+        c = torch.empty((rows, n_out), dtype=torch.uint8, device=a.device)
+        c_scales = torch.empty((rows, n_out // 32), dtype=torch.uint8, device=a.device)
+    else:
+        c = torch.empty((rows, n_out), dtype=torch.float32 if c_dt == 0 else torch.bfloat16, device=a.device)
     args = GemmArgs(a=a.data_ptr(), a_scales=a_scales.data_ptr() if a_scales is not None else None,
                     a_gather=a_gather.data_ptr() if a_gather is not None else None,
                     w_packed=w_packed.data_ptr(), w_scales=w_scales.data_ptr(),
-                    expert_offsets=expert_offsets.data_ptr(), c=c.data_ptr(), c_scales=None,
+                    expert_offsets=expert_offsets.data_ptr(), c=c.data_ptr(),
+                    c_scales=c_scales.data_ptr() if c_scales is not None else None,
                     a_dtype=1 if a_scales is not None else 0, a_gather_div=a_gather_div,
                     a_rows=a.shape[0], rows=rows, E=E, N=N, K=K, epilogue=epi, c_dtype=c_dt)
     n = lib.moe_grouped_gemm_workspace_size(ctypes.byref(args))
     ws = _u8(n, a.device)
     _check(lib.moe_mxfp4_grouped_gemm(ctypes.byref(args), _ptr(ws), n, _stream(stream)))
-    return c
+    return (c, c_scales) if c_dt == 2 else c
 
 
 def combine(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor, *, rms_next: bool = False,
@@ -196,16 +204,19 @@ def combine(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor, *, rm
 class Layer:
     """A resident layer: weights stay on the device; forward() runs the five steps on one stream."""
 
-    def __init__(self, w1_packed, w1_scales, w2_packed, w2_scales, k: int, layout: str = "split"):
+    def __init__(self, w1_packed, w1_scales, w2_packed, w2_scales, k: int, layout: str = "split",
+                 inter: str = "bf16"):
+        """inter: precision of the SwiGLU output fed to FC2, "bf16" or "mxfp8"."""
         self.w1p, self.w1s, self.w2p, self.w2s = w1_packed, w1_scales, w2_packed, w2_scales
         self.E, two_i, h2 = w1_packed.shape
         self.I, self.H = two_i // 2, 2 * h2
         self.k = k
         self.layout = LAYOUT[layout]
+        self.inter = OUT[{"bf16": "MOE_OUT_BF16", "mxfp8": "MOE_OUT_MXFP8_E4M3"}[inter]]
         self._ws = None
 
     def workspace_bytes(self, T: int) -> int:
-        return lib.moe_layer_workspace_size(T, self.H, self.I, self.E, self.k, OUT["MOE_OUT_BF16"])
+        return lib.moe_layer_workspace_size(T, self.H, self.I, self.E, self.k, self.inter)
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, x_scales: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, x_next: Optional[torch.Tensor] = None, stream=None):
@@ -216,7 +227,7 @@ class Layer:
         if out is None:
             out = torch.empty((T, self.H), dtype=torch.float32, device=logits.device)
         args = LayerArgs(T=T, H=self.H, I=self.I, E=self.E, k=self.k, layout=self.layout,
-                         act_dtype=1 if x_scales is not None else 0, inter_dtype=OUT["MOE_OUT_BF16"],
+                         act_dtype=1 if x_scales is not None else 0, inter_dtype=self.inter,
                          logits=logits.data_ptr(), x=x.data_ptr(),
                          x_scales=x_scales.data_ptr() if x_scales is not None else None,
                          w1_packed=self.w1p.data_ptr(), w1_scales=self.w1s.data_ptr(),
@@ -229,7 +240,7 @@ class Layer:
     def routing(self, T: int):
         """Views of the routing arrays the last forward() wrote into its workspace."""
         def view(which, count, dtype):
-            off = lib.moe_layer_workspace_offset(T, self.H, self.I, self.E, self.k, OUT["MOE_OUT_BF16"], which)
+            off = lib.moe_layer_workspace_offset(T, self.H, self.I, self.E, self.k, self.inter, which)
             return self._ws[off: off + 4 * count].view(dtype)
         Tk = T * self.k
         return dict(ids=view(0, Tk, torch.int32).view(T, self.k), w=view(1, Tk, torch.float32).view(T, self.k),

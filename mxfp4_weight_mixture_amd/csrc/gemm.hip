@@ -39,6 +39,8 @@
 // applies to K block g of its row/column.  For the bf16 32x32x16 MFMA a
 // lane in half g holds K [8g, 8g+8).  Accumulator j of lane l is
 // C[8*(j/4) + 4*(l/32) + j%4][l % 32].
+#include <type_traits>
+
 #include "internal.h"
 
 namespace mxmoe {
@@ -69,6 +71,7 @@ struct Params {
   const uint8_t* w_scales;
   const int32_t* offsets;
   void* c;
+  uint8_t* c_scales;   // E8M0 [rows][n_out / 32], MXFP8 output only
   const Tile* tiles;
   const int32_t* tile_count;
   int a_gather_div;
@@ -112,17 +115,14 @@ struct Cfg {
 // Row of W (within one expert) that feeds tile column j of n-tile nt.
 template <int WN>
 __device__ inline int w_row_of(int layout, int nt, int j, int N, int n_out) {
-  if (layout == 0) {
-    const int n = nt * kBN + j;
-    return n < N ? n : N - 1;
-  }
-  // SwiGLU: each wave's WN columns are WN/2 gate rows then the WN/2 matching up rows
+  if (layout == 0) return min(nt * kBN + j, N - 1);
+  // SwiGLU: each wave's WN columns are WN/2 gate rows then the WN/2 matching up
+  // rows (selects only: the lane-dependent part has no branches)
   const int hp = WN / 2;
   const int i = nt * (kBN / 2) + (j / WN) * hp + (j % WN) % hp;
-  const bool up = (j % WN) >= hp;
-  if (i >= n_out) return 0;
-  if (layout == 1) return up ? n_out + i : i;
-  return up ? 2 * i + 1 : 2 * i;
+  const int up = (j % WN) >= hp ? 1 : 0;
+  const int r = layout == 1 ? i + up * n_out : 2 * i + up;
+  return i < n_out ? r : 0;
 }
 
 template <int BM, bool FP8, int EPI, int OUT>
@@ -420,8 +420,17 @@ __device__ __forceinline__ int a_swz(int r) {
 }
 __device__ __forceinline__ int b_swz(int line) { return ((line >> 1) & 3) ^ ((line & 1) << 1); }
 
-__device__ __forceinline__ void lds_dma16(const void* g, void* l) {
-  __builtin_amdgcn_global_load_lds(g, l, 16, 0, 0);
+// Raw buffer resource over [base, base + 4 GiB).  The DMA below addresses
+// with a 32-bit per-lane offset plus a uniform (scalar) stage offset, which
+// keeps one VGPR per load stream and no 64-bit address arithmetic in the
+// loop; the host bounds every offset below 2^32.
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffff, 0x00020000);
+}
+
+// 16 bytes per lane, global -> LDS (lane i writes dst + 16 i)
+__device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, uint32_t soff, void* dst) {
+  __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
 template <int N>
@@ -431,27 +440,59 @@ __device__ __forceinline__ void wait_vm() {
   __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
 }
 
+__device__ __forceinline__ void wait_lgkm0() {
+  // s_waitcnt lgkmcnt(0), vmcnt and expcnt left at their maxima
+  __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
+}
+
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }
 
+__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+
+// fp32 -> E4M3 code, round to nearest even; |x| <= 448 or NaN (the MXFP8
+// scale below guarantees the bound).  Normal range: round the fp32
+// significand to 3 bits in integer arithmetic; below 2^-6: multiples of 2^-9.
+__device__ inline uint32_t e4m3_rne(float x) {
+  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
+  const float a = fabsf(x);
+  if (a != a) return 0x7fu;
+  uint32_t code;
+  if (a < 0.015625f) {
+    code = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8 (8 = smallest normal)
+  } else {
+    const uint32_t b = __float_as_uint(a);
+    const uint32_t r = b + 0x7ffffu + ((b >> 20) & 1u);
+    code = (r >> 20) - (120u << 3);
+  }
+  return sign | code;
+}
+
+// E8M0 exponent X of one MXFP8 block: the smallest X with amax * 2^-X <= 448
+// (448 = 0.875 * 2^9), clamped to the E8M0 range; amax = 0 gives -127.
+__device__ inline int mxfp8_block_exp(float amax) {
+  if (!(amax > 0.0f)) return -127;
+  int e;
+  const float f = frexpf(amax, &e);   // amax = f * 2^e, f in [0.5, 1)
+  const int x = f <= 0.875f ? e - 9 : e - 8;
+  return x < -127 ? -127 : (x > 127 ? 127 : x);
+}
+
+// One persistent block walks (tile, n-tile) units.  Per unit, the K loop runs
+// over 128-element stages through three LDS stage buffers filled by DMA two
+// stages ahead.  FP8 operands: the stage's fragments are read into registers
+// half a stage ahead of their products (second k-half during the first
+// half's MFMAs, next stage's first k-half during the second half's), with
+// one barrier in the middle of each stage that both publishes stage s+1 and
+// frees stage s's buffer for the DMA of stage s+3.  bf16 operands: the
+// stage's reads and products follow one barrier at its start.
 template <int BM, bool FP8, int EPI, int OUT>
 __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
   using C = Cfg2<BM, FP8>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_TOTAL];
-
-  const int tid = threadIdx.x;
-  const int lane = tid & 63;
-  const int wave = tid >> 6;
-  const int wm0 = (wave / C::WAVES_N) * C::WM;
-  const int wn0 = (wave % C::WAVES_N) * C::WN;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-  // fragment rows / lines start at multiples of 16, so the swizzles depend on the lane only
-  const int xa = a_swz<FP8>(l32 & 15);
-  const int xb = b_swz((l32 >> 1) & 7);
 
   const int count = *p.tile_count;
   const int units = count * p.n_tiles;
@@ -467,6 +508,22 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
   const int nst = K / C::KS;
 
   for (int u = xcd * per_xcd + slot; u < u_end; u += slots) {
+    // Lane-derived values are recomputed per unit from an opaque copy of the
+    // thread index.  Hoisted out of the unit loop they stay live across it and
+    // get spilled, and a spill reload in the pipeline prologue would wait for
+    // every DMA in flight.
+    int tid;
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / C::WAVES_N) * C::WM;
+    const int wn0 = (wave % C::WAVES_N) * C::WN;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    // fragment rows / lines start at multiples of 16, so the swizzles depend on the lane only
+    const int xa = a_swz<FP8>(l32 & 15);
+    const int xb = b_swz((l32 >> 1) & 7);
+
     // units in groups of up to 4 row tiles x all n-tiles, row tile fastest, so
     // that concurrent blocks of one XCD share both their A rows and their B tiles
     constexpr int GM = 4;
@@ -482,52 +539,68 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
     const int mrows = min(BM, p.offsets[e + 1] - row0);
     const size_t w_expert = (size_t)e * p.N;
 
-    // ---- per-lane DMA sources (stage 0; stage s adds s * bytes-per-stage) ----
-    const uint8_t* a_src[C::A_I];
+    // ---- DMA sources: uniform bases, 32-bit per-lane byte offsets (stage 0) ----
+    // gathered A rows: offsets from the start of A; contiguous A rows: from the tile's first row
+    const bool gather = p.a_gather != nullptr;
+    const uint8_t* const a_base = gather ? p.a : p.a + (size_t)row0 * a_row_bytes;
+    uint32_t a_off[C::A_I];
+    {
+      int arow[C::A_I];
 #pragma unroll
-    for (int i = 0; i < C::A_I; ++i) {
-      const int r = (wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA;
-      const int chunk = (lane % C::SA) ^ a_swz<FP8>(r);
-      const int grow = row0 + min(r, mrows - 1);
-      const int arow = p.a_gather ? p.a_gather[grow] / p.a_gather_div : grow;
-      a_src[i] = p.a + (size_t)arow * a_row_bytes + chunk * 16;
+      for (int i = 0; i < C::A_I; ++i)
+        arow[i] = min((wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA, mrows - 1);
+      if (gather) {
+        // all index loads in flight together
+#pragma unroll
+        for (int i = 0; i < C::A_I; ++i) arow[i] = p.a_gather[row0 + arow[i]];
+#pragma unroll
+        for (int i = 0; i < C::A_I; ++i) arow[i] /= p.a_gather_div;
+      }
+#pragma unroll
+      for (int i = 0; i < C::A_I; ++i) {
+        const int r = (wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA;
+        const int chunk = (lane % C::SA) ^ a_swz<FP8>(r);
+        a_off[i] = (uint32_t)arow[i] * (uint32_t)a_row_bytes + chunk * 16;
+      }
     }
-    const uint8_t* b_src[C::B_I];
+    const uint8_t* const b_base = p.w + w_expert * (size_t)(K / 2);
+    uint32_t b_off[C::B_I];
 #pragma unroll
     for (int i = 0; i < C::B_I; ++i) {
       const int line = (wave * C::B_I + i) * 8 + lane / 8;
       const int uu = (lane & 7) ^ b_swz(line);
       const int j = line * 2 + (uu >> 2);
       const int wr = w_row_of<C::WN>(p.layout, nt, j, p.N, p.n_out);
-      b_src[i] = p.w + (w_expert + wr) * (size_t)(K / 2) + (uu & 3) * 16;
+      b_off[i] = (uint32_t)wr * (uint32_t)(K / 2) + (uu & 3) * 16;
     }
     const int srow = wave * 64 + lane;   // scale row this lane loads (A: if < BM)
-    const uint8_t* as_src = nullptr;
+    const uint8_t* const as_base = gather ? p.a_scales : p.a_scales + (size_t)row0 * kb;
+    uint32_t as_off = 0;
     if (FP8 && srow < BM) {
-      const int grow = row0 + min(srow, mrows - 1);
-      const int arow = p.a_gather ? p.a_gather[grow] / p.a_gather_div : grow;
-      as_src = p.a_scales + (size_t)arow * kb;
+      const int r = min(srow, mrows - 1);
+      as_off = (uint32_t)(gather ? p.a_gather[row0 + r] / p.a_gather_div : r) * (uint32_t)kb;
     }
-    const uint8_t* bs_src =
-        p.w_scales + (w_expert + w_row_of<C::WN>(p.layout, nt, srow, p.N, p.n_out)) * (size_t)kb;
+    const uint8_t* const bs_base = p.w_scales + w_expert * (size_t)kb;
+    const uint32_t bs_off = (uint32_t)w_row_of<C::WN>(p.layout, nt, srow, p.N, p.n_out) * (uint32_t)kb;
     uint8_t* const sg = lds + C::NST * C::LDS_STAGE;   // two scale groups
 
+    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
+    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
+    const __amdgpu_buffer_rsrc_t ras = make_rsrc(as_base);
+    const __amdgpu_buffer_rsrc_t rbs = make_rsrc(bs_base);
     auto issue = [&](int s) {
       uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
 #pragma unroll
-      for (int i = 0; i < C::A_I; ++i)
-        lds_dma16(a_src[i] + (size_t)s * C::RA, base + (wave * C::A_I + i) * 1024);
+      for (int i = 0; i < C::A_I; ++i) dma16(ra, a_off[i], s * C::RA, base + (wave * C::A_I + i) * 1024);
 #pragma unroll
       for (int i = 0; i < C::B_I; ++i)
-        lds_dma16(b_src[i] + (size_t)s * C::RB, base + C::LDS_A + (wave * C::B_I + i) * 1024);
+        dma16(rb, b_off[i], s * C::RB, base + C::LDS_A + (wave * C::B_I + i) * 1024);
     };
     // scale group j (stages 4j..4j+3): 16 bytes of every A and B row
     auto issue_scales = [&](int j) {
       uint8_t* base = sg + (j & 1) * C::LDS_SG;
-      if (FP8 && wave * 64 < BM) {
-        if (as_src) lds_dma16(as_src + 16 * j, base + wave * 1024);
-      }
-      lds_dma16(bs_src + 16 * j, base + C::SG_A + wave * 1024);
+      if (FP8 && wave * 64 < BM) dma16(ras, as_off, 16 * j, base + wave * 1024);
+      dma16(rbs, bs_off, 16 * j, base + C::SG_A + wave * 1024);
     };
 
     v16f acc[C::FM][C::FN];
@@ -538,63 +611,154 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
 #pragma unroll
         for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
 
-    issue_scales(0);
-    issue(0);
-    if (nst > 1) issue(1);
-
-    for (int s = 0; s < nst; ++s) {
-      // loads issued after stage s's: stage s+1's (and possibly a scale group); waiting
-      // for fewer outstanding than that is conservative
-      if (s + 1 < nst) wait_vm<C::LOADS>();
-      else wait_vm<0>();
-      stage_barrier();
-      if (s + 2 < nst) {
-        issue(s + 2);
-        if (((s + 2) & 3) == 0) issue_scales((s + 2) >> 2);
-      }
-      const uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
-      const uint8_t* la = base;
-      const uint8_t* lb = base + C::LDS_A;
-      const uint8_t* lsg = sg + ((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4;
-      const uint8_t* lsa = lsg;
-      const uint8_t* lsb = lsg + C::SG_A;
-      // four scale bytes (this stage's blocks) per fragment row / column
-      uint32_t bsw[C::FN];
-#pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn)
-        bsw[fn] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + fn * 32 + l32) * 16);
-      if constexpr (FP8) {
-        uint32_t asw[C::FM];
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-          asw[fm] = *reinterpret_cast<const uint32_t*>(lsa + (wm0 + fm * 32 + l32) * 16);
-#pragma unroll
-        for (int kk = 0; kk < 2; ++kk) {
-          v8i af[C::FM];
-#pragma unroll
-          for (int fm = 0; fm < C::FM; ++fm) {
-            const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
-            // K [kk*64 + 16g, +16) and [kk*64 + 32 + 16g, +16): chunks 4kk+g and 4kk+2+g
-            const v4i lo = *reinterpret_cast<const v4i*>(row + (((4 * kk + g) ^ xa) << 4));
-            const v4i hi = *reinterpret_cast<const v4i*>(row + (((4 * kk + 2 + g) ^ xa) << 4));
-            af[fm] = v8i{lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-          }
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) {
-            const int n = wn0 + fn * 32 + l32;
-            const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xb;
-            const v4i bq = *reinterpret_cast<const v4i*>(lb + (n >> 1) * 128 + (uu << 4));
-            const v8i bf = v8i{bq[0], bq[1], bq[2], bq[3], 0, 0, 0, 0};
-            const int bsc = (bsw[fn] >> (8 * (2 * kk + g))) & 0xff;
-#pragma unroll
-            for (int fm = 0; fm < C::FM; ++fm) {
-              const int asc = (asw[fm] >> (8 * (2 * kk + g))) & 0xff;
-              acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
-                  af[fm], bf, acc[fm][fn], 0 /*A: fp8 e4m3*/, 4 /*B: fp4 e2m1*/, 0, asc, 0, bsc);
-            }
+    if constexpr (FP8) {
+      uint32_t sa[C::FM], sb[C::FN], na[C::FM], nb[C::FN];
+      v8i a0[C::FM], a1[C::FM];
+      v4i b0[C::FN], b1[C::FN];
+      // LDS base of stage s, made opaque to the compiler: otherwise every
+      // fragment address becomes an induction variable of its own
+      auto stage_lds = [&](int s) {
+        return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
+      };
+      // read j of one k-half: j < FN: B fragment j; then the A fragments' low and high halves
+      // (A: K [kk*64 + 16g, +16) and [kk*64 + 32 + 16g, +16) = chunks 4kk+g and 4kk+2+g)
+      auto read_frag = [&](int s, int kk, int j, v8i (&af)[C::FM], v4i (&bq)[C::FN]) {
+        const uint8_t* la = stage_lds(s);
+        if (j < C::FN) {
+          const int n = wn0 + j * 32 + l32;
+          const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xb;
+          bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
+        } else {
+          const int fm = (j - C::FN) >> 1, hi = (j - C::FN) & 1;
+          const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
+          const v4i v = *reinterpret_cast<const v4i*>(row + (((4 * kk + 2 * hi + g) ^ xa) << 4));
+          if (hi) {
+            af[fm][4] = v[0]; af[fm][5] = v[1]; af[fm][6] = v[2]; af[fm][7] = v[3];
+          } else {
+            af[fm][0] = v[0]; af[fm][1] = v[1]; af[fm][2] = v[2]; af[fm][3] = v[3];
           }
         }
-      } else {
+      };
+      // scale word j of stage s: four E8M0 bytes (the stage's blocks) of an A row or B column
+      auto read_scale = [&](int s, int j, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
+        const uint8_t* lsg = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4);
+        if (j < C::FM) ta[j] = *reinterpret_cast<const uint32_t*>(lsg + (wm0 + j * 32 + l32) * 16);
+        else tb[j - C::FM] = *reinterpret_cast<const uint32_t*>(lsg + C::SG_A + (wn0 + (j - C::FM) * 32 + l32) * 16);
+      };
+      // product i of one k-half, B-fragment major
+      auto mma = [&](int kk, int i, const v8i (&af)[C::FM], const v4i (&bq)[C::FN], const uint32_t (&ta)[C::FM],
+                     const uint32_t (&tb)[C::FN]) {
+        const int fn = i / C::FM, fm = i % C::FM;
+        const v8i bf = v8i{bq[fn][0], bq[fn][1], bq[fn][2], bq[fn][3], 0, 0, 0, 0};
+        const int bsc = (tb[fn] >> (8 * (2 * kk + g))) & 0xff;
+        const int asc = (ta[fm] >> (8 * (2 * kk + g))) & 0xff;
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0 /*A: fp8 e4m3*/,
+                                                                      4 /*B: fp4 e2m1*/, 0, asc, 0, bsc);
+      };
+      constexpr int MF = C::FM * C::FN;
+      constexpr int NR = 2 * C::FM + C::FN;   // fragment reads of one k-half
+      constexpr int NS = C::FM + C::FN;       // scale reads of one stage
+      // reads issued after each product: at least two (front-loaded), more for small tiles
+      constexpr int R1 = (NR + MF - 1) / MF > 2 ? (NR + MF - 1) / MF : 2;
+      constexpr int R2 = (NR + NS + MF - 1) / MF > 2 ? (NR + NS + MF - 1) / MF : 2;
+      // One stage.  ISSUE: refill the freed buffer with stage s+3 (SCALES: and the
+      // next scale group); WAIT: vmcnt allowance at the mid-stage barrier, -1 for
+      // the last stage (no barrier, no next-stage reads).  All three are compile-time
+      // constants so that the loop body has no branch the compiler could sink the
+      // first half's products past.  Every group of one product and its reads is
+      // fenced with sched_barrier to keep the interleave.
+      auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, const uint32_t (&ta)[C::FM],
+                      const uint32_t (&tb)[C::FN], uint32_t (&tna)[C::FM], uint32_t (&tnb)[C::FN]) {
+        constexpr bool kIssue = decltype(ISSUE)::value;
+        constexpr bool kScales = decltype(SCALES)::value;
+        constexpr int kWait = decltype(WAIT)::value;
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+          mma(0, i, a0, b0, ta, tb);
+          __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+          for (int r = R1 * i; r < R1 * i + R1; ++r)
+            if (r < NR) read_frag(s, 1, r, a1, b1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the first half's products stay ahead of the barrier
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
+        if constexpr (kWait >= 0) {
+          // stage s fully read by this wave; stage s+1 landed for this wave's loads
+          wait_lgkm0();
+          wait_vm<kWait>();
+          stage_barrier();
+          if constexpr (kIssue) {
+            issue(s + 3);
+            if constexpr (kScales) issue_scales((s + 3) >> 2);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+          mma(1, i, a1, b1, ta, tb);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kWait >= 0) {
+#pragma unroll
+            for (int r = R2 * i; r < R2 * i + R2; ++r) {
+              if (r < NS) read_scale(s + 1, r, tna, tnb);
+              else if (r < NS + NR) read_frag(s + 1, 0, r - NS, a0, b0);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      using T = std::integral_constant<bool, true>;
+      using F = std::integral_constant<bool, false>;
+      using WL = std::integral_constant<int, C::LOADS>;   // stage s+2 may still be in flight
+      issue_scales(0);
+      issue(0);
+      issue(1);
+      issue(2);
+      wait_vm<2 * C::LOADS>();
+      stage_barrier();
+#pragma unroll
+      for (int r = 0; r < NS; ++r) read_scale(0, r, sa, sb);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) read_frag(0, 0, r, a0, b0);
+      // the stage count is a multiple of four (K % 512 == 0): groups of four stages,
+      // the last group with its tail conditions resolved at compile time
+      int s = 0;
+      for (; s + 4 < nst; s += 4) {
+        step(s, T{}, F{}, WL{}, sa, sb, na, nb);
+        step(s + 1, T{}, T{}, WL{}, na, nb, sa, sb);
+        step(s + 2, T{}, F{}, WL{}, sa, sb, na, nb);
+        step(s + 3, T{}, F{}, WL{}, na, nb, sa, sb);
+      }
+      step(s, T{}, F{}, WL{}, sa, sb, na, nb);
+      step(s + 1, F{}, F{}, WL{}, na, nb, sa, sb);
+      step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sa, sb, na, nb);
+      step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, na, nb, sa, sb);
+    } else {
+      issue_scales(0);
+      issue(0);
+      issue(1);
+      for (int s = 0; s < nst; ++s) {
+        // loads issued after stage s's: stage s+1's (and possibly a scale group); waiting
+        // for fewer outstanding than that is conservative
+        if (s + 1 < nst) wait_vm<C::LOADS>();
+        else wait_vm<0>();
+        stage_barrier();
+        if (s + 2 < nst) {
+          issue(s + 2);
+          if (((s + 2) & 3) == 0) issue_scales((s + 2) >> 2);
+        }
+        const uint8_t* la = lds + (s % C::NST) * C::LDS_STAGE;
+        const uint8_t* lb = la + C::LDS_A;
+        const uint8_t* lsb = sg + ((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4 + C::SG_A;
+        // four scale bytes (this stage's blocks) per B column
+        uint32_t bsw[C::FN];
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn)
+          bsw[fn] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + fn * 32 + l32) * 16);
 #pragma unroll
         for (int h = 0; h < 2; ++h) {
           // this lane's 32 weights of block 2h+g, expanded to bf16
@@ -635,45 +799,143 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
     }
 
     // ---- epilogue: registers -> C in permuted row order ----
-    if constexpr (EPI == 0) {
+    // gate/up pairing of the SwiGLU layouts: this wave's fragment fh holds gate
+    // columns, fragment fh + FN/2 the matching up columns
+    constexpr int HF = C::FN / 2;
+    if constexpr (OUT == MOE_OUT_FP32) {
+      // fp32: straight from the accumulators, one fragment at a time
+      if constexpr (EPI == 0) {
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+        for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) {
-          const int n = nt * kBN + wn0 + fn * 32 + l32;
+          for (int fn = 0; fn < C::FN; ++fn) {
+            const int n = nt * kBN + wn0 + fn * 32 + l32;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-            if (r < mrows && n < p.N) {
-              const size_t o = (size_t)(row0 + r) * p.N + n;
-              if (OUT == MOE_OUT_FP32) static_cast<float*>(p.c)[o] = acc[fm][fn][q];
-              else static_cast<uint16_t*>(p.c)[o] = (uint16_t)bf16_rne(acc[fm][fn][q]);
+            for (int q = 0; q < 16; ++q) {
+              const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+              if (r < mrows && n < p.N) static_cast<float*>(p.c)[(size_t)(row0 + r) * p.N + n] = acc[fm][fn][q];
             }
+            __builtin_amdgcn_sched_barrier(0);
           }
-        }
+      } else {
+        const int i_base = nt * (kBN / 2) + (wave % C::WAVES_N) * (C::WN / 2);
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int fh = 0; fh < HF; ++fh) {
+            const int i = i_base + fh * 32 + l32;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+              const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
+              if (r < mrows && i < p.n_out) static_cast<float*>(p.c)[(size_t)(row0 + r) * p.n_out + i] = a;
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
     } else {
-      constexpr int HF = C::FN / 2;
-      const int i_base = nt * (kBN / 2) + (wave % C::WAVES_N) * (C::WN / 2);
+      // bf16 and MXFP8: the tile goes through LDS (row-major, rows padded by 16
+      // bytes) so that the global stores are whole row segments
+      constexpr bool MX = OUT == MOE_OUT_MXFP8_E4M3;
+      static_assert(!MX || EPI != 0, "MXFP8 output needs the SwiGLU epilogue");
+      constexpr int EB = MX ? 4 : 2;                   // bytes per staged element
+      constexpr int TC = EPI == 0 ? kBN : kBN / 2;    // tile columns
+      constexpr int PITCH = EB * TC + 16;
+      static_assert(BM * PITCH <= C::LDS_TOTAL, "C tile must fit in LDS");
+      stage_barrier();   // every wave is done reading the stage buffers
+      if constexpr (EPI == 0) {
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+        for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int fh = 0; fh < HF; ++fh) {
-          const int i = i_base + fh * 32 + l32;
+          for (int fn = 0; fn < C::FN; ++fn) {
+            uint8_t* col = lds + (wn0 + fn * 32 + l32) * 2;
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-            const float gv = acc[fm][fh][q];
-            const float uv = acc[fm][fh + HF][q];
-            const float a = __fdividef(gv, 1.0f + __expf(-gv)) * uv;
-            if (r < mrows && i < p.n_out) {
-              const size_t o = (size_t)(row0 + r) * p.n_out + i;
-              if (OUT == MOE_OUT_FP32) static_cast<float*>(p.c)[o] = a;
-              else static_cast<uint16_t*>(p.c)[o] = (uint16_t)bf16_rne(a);
+            for (int q = 0; q < 16; ++q) {
+              const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+              *reinterpret_cast<uint16_t*>(col + r * PITCH) = (uint16_t)bf16_rne(acc[fm][fn][q]);
             }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      } else {
+#pragma unroll
+        for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+          for (int fh = 0; fh < HF; ++fh) {
+            uint8_t* col = lds + ((wave % C::WAVES_N) * (C::WN / 2) + fh * 32 + l32) * EB;
+#pragma unroll
+            for (int q = 0; q < 16; ++q) {
+              const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+              const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
+              if constexpr (MX) *reinterpret_cast<float*>(col + r * PITCH) = a;
+              else *reinterpret_cast<uint16_t*>(col + r * PITCH) = (uint16_t)bf16_rne(a);
+            }
+            __builtin_amdgcn_sched_barrier(0);
+          }
+      }
+      stage_barrier();
+      const int ld = EPI == 0 ? p.N : p.n_out;
+      const int col0 = nt * TC;
+      const int ncols = min(TC, ld - col0);
+      if constexpr (!MX) {
+        const bool vec = ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && (ld % 8 == 0);
+        constexpr int CPR = TC / 8;   // 16-byte chunks per tile row
+        uint16_t* const out = static_cast<uint16_t*>(p.c) + (size_t)row0 * ld + col0;
+        for (int idx = tid; idx < mrows * CPR; idx += kThreads) {
+          const int r = idx / CPR, c = (idx % CPR) * 8;
+          if (c >= ncols) continue;
+          const uint4 v = *reinterpret_cast<const uint4*>(lds + r * PITCH + c * 2);
+          uint16_t* dst = out + (size_t)r * ld + c;
+          if (vec && c + 8 <= ncols) {
+            *reinterpret_cast<uint4*>(dst) = v;
+          } else {
+            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+            for (int j = 0; j < 8; ++j)
+              if (c + j < ncols) dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
           }
         }
+      } else {
+        // one 32-element MX block per thread and step: amax -> E8M0 exponent X ->
+        // E4M3 codes of v * 2^-X; ld is a multiple of 32 (the host checks)
+        const bool vec = (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && ld % 16 == 0;
+        constexpr int BPR = TC / 32;   // blocks per tile row
+        uint8_t* const out = static_cast<uint8_t*>(p.c) + (size_t)row0 * ld + col0;
+        uint8_t* const osc = p.c_scales + (size_t)row0 * (ld / 32) + col0 / 32;
+        for (int idx = tid; idx < mrows * BPR; idx += kThreads) {
+          const int r = idx / BPR, c = (idx % BPR) * 32;
+          if (c >= ncols) continue;
+          const float4* src = reinterpret_cast<const float4*>(lds + r * PITCH + c * 4);
+          float v[32];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            const float4 f = src[j];
+            v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+          }
+          float amax = 0.f;
+#pragma unroll
+          for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+          const int x = mxfp8_block_exp(amax);
+          uint32_t w[8];
+#pragma unroll
+          for (int j = 0; j < 8; ++j) {
+            uint32_t q = 0;
+#pragma unroll
+            for (int t = 0; t < 4; ++t) q |= e4m3_rne(ldexpf(v[4 * j + t], -x)) << (8 * t);
+            w[j] = q;
+          }
+          uint8_t* dst = out + (size_t)r * ld + c;
+          if (vec) {
+            reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+            reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+          } else {
+#pragma unroll
+            for (int j = 0; j < 32; ++j) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+          }
+          osc[(size_t)r * (ld / 32) + c / 32] = (uint8_t)(x + 127);
+        }
+      }
     }
-    // every wave is done reading the stage buffers before the next unit refills them
+    // every wave is done with LDS before the next unit refills it
     stage_barrier();
   }
 }
@@ -801,7 +1063,9 @@ moe_status dispatch_out(const Params& p, int c_dtype, const Tile* lists, int cap
                         const int32_t* counts, hipStream_t s) {
   if (c_dtype == MOE_OUT_FP32) return launch_all<FP8, EPI, MOE_OUT_FP32, DMA>(p, lists, cap, counts, s);
   if (c_dtype == MOE_OUT_BF16) return launch_all<FP8, EPI, MOE_OUT_BF16, DMA>(p, lists, cap, counts, s);
-  return fail(MOE_ERR_NOT_IMPLEMENTED, "grouped GEMM: MXFP8 output is not provided by this build");
+  if constexpr (DMA && EPI != 0) return launch_all<FP8, EPI, MOE_OUT_MXFP8_E4M3, DMA>(p, lists, cap, counts, s);
+  return fail(MOE_ERR_NOT_IMPLEMENTED,
+              "grouped GEMM: MXFP8 output needs the SwiGLU epilogue and K %% 512 == 0");
 }
 
 template <bool FP8, bool DMA>
@@ -836,8 +1100,22 @@ moe_status validate_gemm(const moe_gemm_args& a) {
     return fail(MOE_ERR_SHAPE, "grouped GEMM: K (%d) and N (%d) must be multiples of 32", a.K, a.N);
   if (a.epilogue != MOE_EPI_NONE && a.N % 64)
     return fail(MOE_ERR_SHAPE, "grouped GEMM: a SwiGLU epilogue needs N %% 64 == 0 (gate + up), got %d", a.N);
-  if (a.c_dtype == MOE_OUT_MXFP8_E4M3)
-    return fail(MOE_ERR_NOT_IMPLEMENTED, "grouped GEMM: MXFP8 output is not provided by this build");
+  if (a.c_dtype == MOE_OUT_MXFP8_E4M3) {
+    if (a.epilogue == MOE_EPI_NONE || a.K % 512)
+      return fail(MOE_ERR_NOT_IMPLEMENTED,
+                  "grouped GEMM: MXFP8 output needs the SwiGLU epilogue and K %% 512 == 0 (K = %d)", a.K);
+    if (!a.c_scales) return fail(MOE_ERR_INVALID_ARG, "grouped GEMM: MXFP8 output needs c_scales");
+  }
+  if (a.K % 512 == 0) {
+    // the DMA kernels address with 32-bit offsets: from the start of a gathered A,
+    // from an expert's first weight row
+    const uint64_t a_bytes = (uint64_t)a.a_rows * a.K * (a.a_dtype == MOE_ACT_MXFP8_E4M3 ? 1 : 2);
+    if (a.a_gather && a_bytes >= (1ull << 32))
+      return fail(MOE_ERR_SHAPE, "grouped GEMM: a gathered A of %llu bytes exceeds 4 GiB",
+                  (unsigned long long)a_bytes);
+    if ((uint64_t)a.N * (a.K / 2) >= (1ull << 32))
+      return fail(MOE_ERR_SHAPE, "grouped GEMM: one expert's weights exceed 4 GiB");
+  }
   if (!a.a_gather && a.a_rows < a.rows)
     return fail(MOE_ERR_SHAPE, "grouped GEMM: A has %d rows, fewer than rows %d", a.a_rows, a.rows);
   return MOE_OK;
@@ -867,6 +1145,7 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
   p.w_scales = a.w_scales;
   p.offsets = a.expert_offsets;
   p.c = a.c;
+  p.c_scales = a.c_scales;
   p.N = a.N;
   p.K = a.K;
   p.layout = a.epilogue;

@@ -51,8 +51,8 @@ moe_status validate_layer_sizes(int T, int H, int I, int E, int k, int layout, i
     return fail(MOE_ERR_INVALID_ARG, "layer: bad act_dtype %d", act);
   if (inter != MOE_OUT_BF16 && inter != MOE_OUT_MXFP8_E4M3)
     return fail(MOE_ERR_INVALID_ARG, "layer: inter_dtype %d must be MOE_OUT_BF16 or MOE_OUT_MXFP8_E4M3", inter);
-  if (inter == MOE_OUT_MXFP8_E4M3)
-    return fail(MOE_ERR_NOT_IMPLEMENTED, "layer: an MXFP8 intermediate is not provided by this build");
+  if (inter == MOE_OUT_MXFP8_E4M3 && H % 512)
+    return fail(MOE_ERR_NOT_IMPLEMENTED, "layer: an MXFP8 intermediate needs H %% 512 == 0 (H = %d)", H);
   if ((int64_t)T * k >= (1ll << 31)) return fail(MOE_ERR_SHAPE, "layer: T*k overflows int32");
   return MOE_OK;
 }

@@ -97,3 +97,58 @@ def dequant_mxfp8(codes, scales):
     K = c.shape[-1]
     vals = E4M3_TABLE[c].reshape(c.shape[:-1] + (K // 32, 32))
     return (vals * E8M0_TABLE[s][..., None]).reshape(c.shape)
+
+
+# --- MXFP8 encoding of the layer's intermediate ------------------------------
+# The pages leave the precision of the SwiGLU output fed to FC2 open; the
+# MXFP8 x MXFP4 product they describe ("Kimi-K3 SM120 FlashInfer MXFP4 MoE",
+# goal section) is read as taking MXFP8 operands on both GEMMs.  The block
+# scale is chosen so that no element saturates: the smallest exponent X with
+# amax * 2**-X <= 448, the E4M3 maximum.  Elements round to the nearest E4M3
+# value, ties to the even code (the OCP specification's default rounding).
+
+_E4M3_POS = E4M3_TABLE[:127]   # codes 0x00..0x7E: the finite non-negative values, ascending
+
+
+def mxfp8_block_exponent(amax):
+    """Smallest integer X with amax * 2**-X <= 448, clamped to [-127, 127]; amax == 0 -> -127."""
+    amax = float(amax)
+    if not amax > 0.0:
+        return -127
+    x = int(np.ceil(np.log2(amax / 448.0)))
+    # settle the floating-point guess against the exact power-of-two test
+    while np.ldexp(amax, -x) > 448.0:
+        x += 1
+    while np.ldexp(amax, -(x - 1)) <= 448.0:
+        x -= 1
+    return max(-127, min(127, x))
+
+
+def e4m3_nearest(v):
+    """float64 value(s) with |v| <= 448 -> nearest E4M3 code, ties to the even code."""
+    v = np.asarray(v, dtype=np.float64)
+    a = np.abs(v)
+    hi = np.clip(np.searchsorted(_E4M3_POS, a, side="left"), 0, 126)   # first value >= a
+    lo = np.clip(hi - 1, 0, 126)
+    dlo = a - _E4M3_POS[lo]
+    dhi = _E4M3_POS[hi] - a
+    pick_hi = (dhi < dlo) | ((dhi == dlo) & (hi % 2 == 0))
+    code = np.where(pick_hi, hi, lo).astype(np.int64)
+    return np.where(np.signbit(v), code | 0x80, code).astype(np.uint8)
+
+
+def quantize_mxfp8(values):
+    """[..., K] values (K % 32 == 0) -> (E4M3 codes [..., K], E8M0 bytes [..., K/32])."""
+    v = np.asarray(values, dtype=np.float64)
+    K = v.shape[-1]
+    if K % 32:
+        raise ValueError("K must be a multiple of 32")
+    blocks = v.reshape(-1, K // 32, 32)
+    codes = np.empty(blocks.shape, dtype=np.uint8)
+    scales = np.empty(blocks.shape[:2], dtype=np.uint8)
+    for i in range(blocks.shape[0]):
+        for b in range(blocks.shape[1]):
+            x = mxfp8_block_exponent(np.max(np.abs(blocks[i, b])))
+            scales[i, b] = x + 127
+            codes[i, b] = e4m3_nearest(np.ldexp(blocks[i, b], -x))
+    return codes.reshape(v.shape), scales.reshape(v.shape[:-1] + (K // 32,))

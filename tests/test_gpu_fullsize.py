@@ -29,12 +29,12 @@ def pick_tokens(ids, n):
     return np.array(chosen)
 
 
-def _full(name, n_sample, tol, **over):
+def _full(name, n_sample, tol, inter="bf16", **over):
     t0 = time.time()
     s = gen.preset(name, **over)
     li = gen.layer_inputs(s)
     w = device_weights(s)
-    layer = mx.Layer(*w, k=s.k, layout=s.layout)
+    layer = mx.Layer(*w, k=s.k, layout=s.layout, inter=inter)
     x, xs = device_x(li)
     out = layer.forward(torch.from_numpy(li.logits).to(DEV), x, xs)
     torch.cuda.synchronize()
@@ -42,7 +42,7 @@ def _full(name, n_sample, tol, **over):
     out = out.cpu().numpy()
     del w, layer, x, xs
     torch.cuda.empty_cache()
-    print(f"[{name}] gpu done {time.time() - t0:.1f}s", flush=True)
+    print(f"[{name} inter={inter}] gpu done {time.time() - t0:.1f}s", flush=True)
 
     rid, rw = omoe.route(li.logits, s.k)
     np.testing.assert_array_equal(r["ids"], rid)
@@ -57,13 +57,17 @@ def _full(name, n_sample, tol, **over):
     xa = x_as_f64(li)
     ref = omoe.moe_tokens(xa[toks], rid[toks], rw[toks], cpu_weights(s), s.layout)
     err = rel_err(out[toks], ref)
-    print(f"[{name}] tokens {toks.tolist()} experts {len(np.unique(rid[toks]))} "
+    print(f"[{name} inter={inter}] tokens {toks.tolist()} experts {len(np.unique(rid[toks]))} "
           f"rel err {err:.3e} ({time.time() - t0:.1f}s)", flush=True)
     assert err <= tol
 
 
 def test_prefill896_mxfp8_full_size():
     _full("prefill896_mxfp8", 6, 5e-2)
+
+
+def test_prefill896_mxfp8_full_size_mxfp8_intermediate():
+    _full("prefill896_mxfp8", 6, 5e-2, inter="mxfp8")
 
 
 def test_prefill256_full_size():

@@ -187,6 +187,47 @@ def test_gemm_random_against_oracle(fp8, layout, K):
     assert rel_err(c.cpu().numpy(), want) < (1e-4 if fp8 else 1e-5)
 
 
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("layout", ["split", "interleaved"])
+def test_gemm_mxfp8_output_encodes_the_fp32_result(fp8, layout):
+    """The MXFP8 epilogue encodes the same fp32 SwiGLU values the fp32 epilogue
+    writes; the oracle's encoder, given those fp32 values, must produce the same
+    codes and scale bytes (the quantisation decided in the same precision)."""
+    g = np.random.default_rng(12)
+    K, N = 512, 448                                     # N_out = 224: seven blocks per row
+    counts = [300, 0, 5, 129]
+    off = _offsets(counts)
+    rows = int(off[-1])
+    x = torch.from_numpy(g.standard_normal((rows, K)).astype(np.float32)).to(torch.bfloat16)
+    x[7] = 0                                            # a zero row: all-zero blocks
+    wp, ws = _rand_w(len(counts), N, K, seed=5)
+    if fp8:
+        codes, scales = gen.quantize_mxfp8(x.float())
+        a, a_sc = codes.to(DEV), scales.to(DEV)
+    else:
+        a, a_sc = x.to(DEV), None
+    args = (a, torch.from_numpy(wp).to(DEV), torch.from_numpy(ws).to(DEV), torch.from_numpy(off).to(DEV))
+    c32 = mx.grouped_gemm(*args, a_scales=a_sc, epilogue=layout, out_dtype="fp32").cpu().numpy()
+    c8, s8 = mx.grouped_gemm(*args, a_scales=a_sc, epilogue=layout, out_dtype="mxfp8")
+    want_c, want_s = omx.quantize_mxfp8(c32.astype(np.float64))
+    np.testing.assert_array_equal(s8.cpu().numpy(), want_s)
+    got = c8.cpu().numpy()
+    bad = np.argwhere(got != want_c)
+    assert bad.size == 0, f"{len(bad)} code mismatches, first {bad[:5].tolist()}"
+    assert np.all(want_s[7] == 0) and np.all(got[7] == 0)
+
+
+def test_gemm_mxfp8_output_needs_swiglu_and_whole_stages():
+    E, N, K = 1, 128, 256
+    wp, ws = _rand_w(E, N, K, seed=6)
+    a = torch.zeros((4, K), dtype=torch.bfloat16, device=DEV)
+    args = (a, torch.from_numpy(wp).to(DEV), torch.from_numpy(ws).to(DEV), torch.from_numpy(_offsets([4])).to(DEV))
+    for epi in ("none", "split"):                       # no SwiGLU / K % 512 != 0
+        with pytest.raises(mx.MoeError) as ei:
+            mx.grouped_gemm(*args, epilogue=epi, out_dtype="mxfp8")
+        assert ei.value.status == mx.STATUS["MOE_ERR_NOT_IMPLEMENTED"]
+
+
 def test_gemm_bf16_output_rounding():
     g = np.random.default_rng(8)
     E, N, K = 2, 256, 256

@@ -15,17 +15,17 @@ mx = pytest.importorskip("mxfp4_weight_mixture_amd")
 DEV = "cuda"
 
 
-def _run(shape, li, weights=None):
+def _run(shape, li, weights=None, inter="bf16"):
     w = weights if weights is not None else device_weights(shape)
-    layer = mx.Layer(*w, k=shape.k, layout=shape.layout)
+    layer = mx.Layer(*w, k=shape.k, layout=shape.layout, inter=inter)
     x, xs = device_x(li)
     out = layer.forward(torch.from_numpy(li.logits).to(DEV), x, xs)
     torch.cuda.synchronize()
     return out, layer
 
 
-def _check_layer(shape, li, tol):
-    out, layer = _run(shape, li)
+def _check_layer(shape, li, tol, inter="bf16"):
+    out, layer = _run(shape, li, inter=inter)
     ref, it = oracle_layer(shape, li)
     r = {k: v.cpu().numpy() for k, v in layer.routing(shape.T).items()}
     np.testing.assert_array_equal(r["ids"], it["ids"])
@@ -58,6 +58,27 @@ def test_random_shapes(T, H, I, E, k, layout, act):
     s = gen.LayerShape(T=T, H=H, I=I, E=E, k=k, layout=layout, act=act, cfg_id=100 + T)
     li = gen.layer_inputs(s)
     _check_layer(s, li, 2e-2 if act == "bf16" else 5e-2)
+
+
+@pytest.mark.parametrize("T,H,I,E,k,layout,act", [
+    (257, 512, 160, 16, 4, "split", "mxfp8"),       # FC2 with K = 160: register-staged FP8 path
+    (300, 1024, 512, 6, 2, "interleaved", "mxfp8"), # FC2 with K = 512: three-stage DMA FP8 path
+    (64, 512, 256, 3, 2, "split", "bf16"),          # MXFP8 intermediate after bf16 activations
+])
+def test_mxfp8_intermediate(T, H, I, E, k, layout, act):
+    """FC1 writes the SwiGLU output as MXFP8 and FC2 reads it as MXFP8 A: the
+    layer stays within the MXFP8-activation bound of the plain oracle."""
+    s = gen.LayerShape(T=T, H=H, I=I, E=E, k=k, layout=layout, act=act, cfg_id=140 + T)
+    li = gen.layer_inputs(s)
+    _check_layer(s, li, 5e-2, inter="mxfp8")
+
+
+def test_mxfp8_intermediate_needs_h_multiple_of_512():
+    s = gen.preset("tiny")
+    li = gen.layer_inputs(s)
+    with pytest.raises(mx.MoeError) as ei:
+        _run(s, li, inter="mxfp8")
+    assert ei.value.status == mx.STATUS["MOE_ERR_NOT_IMPLEMENTED"]
 
 
 def test_all_tokens_to_one_expert_and_empty_experts():

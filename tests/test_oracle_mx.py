@@ -177,3 +177,57 @@ def test_quantize_mxfp8_is_nearest_even_on_the_grid():
                     assert (c & 1) == 0
     deq = mx.dequant_mxfp8(codes.numpy(), scales.numpy())
     assert np.all(deq[0, :32] == 0)
+
+
+# ---- the oracle's MXFP8 encoder of the intermediate (no-saturation block scale)
+
+def test_intermediate_encoder_round_trips_every_code_at_every_scale():
+    """Every finite E4M3 value times 2**X, placed in a block whose amax pins X,
+    encodes back to its own code and to scale byte X + 127."""
+    grid = mx.e4m3_value(np.arange(256))
+    finite = np.flatnonzero(~np.isnan(grid) & (np.arange(256) != 0x80))
+    for X in (-127, -20, -8, 0, 5, 100):
+        for start in range(0, len(finite), 31):
+            cs = finite[start:start + 31]
+            blk = np.zeros(32)
+            blk[:len(cs)] = np.ldexp(grid[cs], X)
+            blk[31] = np.ldexp(448.0, X)                 # amax = 448 * 2**X exactly
+            codes, scales = mx.quantize_mxfp8(blk[None, :])
+            assert int(scales[0, 0]) == X + 127
+            assert np.array_equal(codes[0, :len(cs)], cs.astype(np.uint8)), X
+            assert codes[0, 31] == 0x7E
+
+
+def test_intermediate_encoder_scale_rule_and_ties():
+    # amax just above 448 * 2**X needs the next exponent; just at it does not
+    for X in (-10, 0, 7):
+        at = np.full((1, 32), np.ldexp(448.0, X))
+        above = at.copy()
+        above[0, 3] = np.nextafter(np.ldexp(448.0, X), np.inf)
+        assert mx.quantize_mxfp8(at)[1][0, 0] == X + 127
+        assert mx.quantize_mxfp8(above)[1][0, 0] == X + 128
+    # an all-zero block: smallest scale, zero codes; a negative zero keeps its sign
+    z = np.zeros((1, 32))
+    z[0, 5] = -0.0
+    codes, scales = mx.quantize_mxfp8(z)
+    assert scales[0, 0] == 0 and codes[0, 0] == 0 and codes[0, 5] == 0x80
+    # midpoints between neighbouring codes go to the even code (amax 448 pins X = 0)
+    grid = mx.e4m3_value(np.arange(0x7F))
+    for c in range(0, 0x7E):
+        mid = (grid[c] + grid[c + 1]) / 2
+        blk = np.array([[mid, -mid] + [0.0] * 29 + [448.0]])
+        codes, _ = mx.quantize_mxfp8(blk)
+        even = c if c % 2 == 0 else c + 1
+        assert codes[0, 0] == even and codes[0, 1] == (even | 0x80), c
+
+
+def test_intermediate_encoder_is_within_half_an_ulp():
+    g = np.random.default_rng(11)
+    v = g.standard_normal((8, 96)) * np.exp(g.uniform(-6, 6, (8, 1)))
+    codes, scales = mx.quantize_mxfp8(v)
+    back = mx.dequant_mxfp8(codes, scales)
+    # E4M3 has 3 mantissa bits: relative error <= 2**-4 for normals; subnormals
+    # are absolute multiples of 2**-9 of the block scale
+    sc = np.repeat(mx.e8m0_value(scales), 32, axis=1)
+    err = np.abs(back - v)
+    assert np.all(err <= np.maximum(np.abs(v) * 2.0 ** -4, sc * 2.0 ** -10) * (1 + 1e-12))
