@@ -56,6 +56,9 @@ def parse():
     p.add_argument("--workload", default="prefill896_mxfp8",
                    choices=["prefill896_mxfp8", "prefill256", "decode", "tiny", "streamed"])
     p.add_argument("--tokens", type=int, default=0, help="override T (decode: 1/2/8/32)")
+    p.add_argument("--inter", default=None, choices=["bf16", "mxfp8"],
+                   help="precision of the SwiGLU output fed to FC2 (default: mxfp8 for MXFP8 "
+                        "activations with hidden % 512 == 0, else bf16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true", help="skip the output checks (profiling runs)")
     return p.parse_args()
@@ -67,8 +70,9 @@ class Steps:
     """The five ABI calls of one layer, with events between them on one stream."""
     NAMES = ["route", "permute", "fc1", "fc2", "combine"]
 
-    def __init__(self, shape, w, x, xs, logits):
+    def __init__(self, shape, w, x, xs, logits, inter="bf16"):
         self.s = shape
+        self.inter = inter
         self.w1p, self.w1s, self.w2p, self.w2s = w
         self.x, self.xs, self.logits = x, xs, logits
         T, k, E, H, I = shape.T, shape.k, shape.E, shape.H, shape.I
@@ -79,7 +83,9 @@ class Steps:
         self.off = torch.empty(E + 1, dtype=torch.int32, device=dev)
         self.ps = torch.empty(rows, dtype=torch.int32, device=dev)
         self.dr = torch.empty(rows, dtype=torch.int32, device=dev)
-        self.act = torch.empty((rows, I), dtype=torch.bfloat16, device=dev)
+        mx8 = inter == "mxfp8"
+        self.act = torch.empty((rows, I), dtype=torch.uint8 if mx8 else torch.bfloat16, device=dev)
+        self.act_s = torch.empty((rows, I // 32), dtype=torch.uint8, device=dev) if mx8 else None
         self.y = torch.empty((rows, H), dtype=torch.bfloat16, device=dev)
         self.out = torch.empty((T, H), dtype=torch.float32, device=dev)
         self.pws_n = mx.lib.moe_permute_workspace_size(T, E, k)
@@ -88,11 +94,13 @@ class Steps:
         self.g1 = mx.GemmArgs(a=x.data_ptr(), a_scales=xs.data_ptr() if xs is not None else None,
                               a_gather=self.ps.data_ptr(), w_packed=self.w1p.data_ptr(),
                               w_scales=self.w1s.data_ptr(), expert_offsets=self.off.data_ptr(),
-                              c=self.act.data_ptr(), c_scales=None, a_dtype=1 if xs is not None else 0,
-                              a_gather_div=k, a_rows=T, rows=rows, E=E, N=2 * I, K=H, epilogue=lay, c_dtype=1)
-        self.g2 = mx.GemmArgs(a=self.act.data_ptr(), a_scales=None, a_gather=None, w_packed=self.w2p.data_ptr(),
-                              w_scales=self.w2s.data_ptr(), expert_offsets=self.off.data_ptr(), c=self.y.data_ptr(),
-                              c_scales=None, a_dtype=0, a_gather_div=1, a_rows=rows, rows=rows, E=E, N=H, K=I,
+                              c=self.act.data_ptr(), c_scales=self.act_s.data_ptr() if mx8 else None,
+                              a_dtype=1 if xs is not None else 0, a_gather_div=k, a_rows=T, rows=rows, E=E,
+                              N=2 * I, K=H, epilogue=lay, c_dtype=2 if mx8 else 1)
+        self.g2 = mx.GemmArgs(a=self.act.data_ptr(), a_scales=self.act_s.data_ptr() if mx8 else None,
+                              a_gather=None, w_packed=self.w2p.data_ptr(), w_scales=self.w2s.data_ptr(),
+                              expert_offsets=self.off.data_ptr(), c=self.y.data_ptr(), c_scales=None,
+                              a_dtype=1 if mx8 else 0, a_gather_div=1, a_rows=rows, rows=rows, E=E, N=H, K=I,
                               epilogue=0, c_dtype=1)
         import ctypes
         self.ctypes = ctypes
@@ -254,7 +262,8 @@ def bench_layer(args):
     torch.cuda.synchronize()
     log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
 
-    steps = Steps(shape, w, x, xs, logits)
+    inter = args.inter or ("mxfp8" if shape.act == "mxfp8" and shape.H % 512 == 0 else "bf16")
+    steps = Steps(shape, w, x, xs, logits, inter)
     steps.run()
     torch.cuda.synchronize()
     ids = steps.ids.cpu().numpy()
@@ -305,7 +314,8 @@ def bench_layer(args):
     else:
         dm = fc1_ms if dom == "fc1" else fc2_ms
         dfl = fc1_flops if dom == "fc1" else fc2_flops
-        pk = fc1_peak if dom == "fc1" else PEAK["bf16_TFLOPs"]
+        fc2_peak = PEAK["fp8_TFLOPs"] if inter == "mxfp8" else PEAK["bf16_TFLOPs"]
+        pk = fc1_peak if dom == "fc1" else fc2_peak
         roof = {"bound": "mfma", "achieved": dfl / (dm * 1e-3) / 1e12, "peak": pk, "unit": "TFLOP/s",
                 "traffic": None, "kernel": f"{dom} grouped GEMM", "per_launch_ms": dm,
                 "algorithmic_per_launch": dfl}
@@ -324,7 +334,8 @@ def bench_layer(args):
         "dtype": "mxfp8xmxfp4" if shape.act == "mxfp8" else "bf16xmxfp4",
         "data": "synthetic",
         "config": {"workload": name, "T": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
-                   "activations": shape.act, "gate_up": shape.layout, "router_bias": shape.bias,
+                   "activations": shape.act, "intermediate_dtype": inter, "gate_up": shape.layout,
+                   "router_bias": shape.bias,
                    "experts_hit": n_hit, "parallelism": "none (1 GPU)"},
         "tflops": tflops,
         "pct_mxfp4_peak": tflops / PEAK["mxfp4_TFLOPs"],
@@ -352,13 +363,23 @@ def bench_streamed(args):
     t0 = time.time()
     blobs = []
     for b in range(n_blobs):
-        blob = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        try:
+            blob = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        except RuntimeError as e:          # the host's pinned-memory limit
+            if b < 2:
+                raise
+            log(f"[bench] streamed: pinned allocation {b + 1} failed ({str(e).splitlines()[0]}); "
+                f"layers reuse {b} blobs")
+            n_blobs = b
+            break
         w = gen.all_expert_weights(shape, b, dev)
         for which, t in enumerate(w):
             o = mx.blob_section_offset(H, I, E, which)
             blob[o:o + t.numel()].copy_(t.reshape(-1))
         del w
         blobs.append(blob)
+        if b % 4 == 3 or b == n_blobs - 1:
+            log(f"[bench] streamed: {b + 1}/{n_blobs} pinned blobs filled ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
     log(f"[bench] streamed: {n_blobs} pinned blobs of {nbytes / 1e9:.3f} GB in {time.time() - t0:.1f}s")
     slots = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
