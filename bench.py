@@ -61,6 +61,9 @@ def parse():
                         "activations with hidden % 512 == 0, else bf16)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true", help="skip the output checks (profiling runs)")
+    p.add_argument("--copy-calibration", action="store_true",
+                   help="only run a 1 GiB device copy three times (the known-size kernel that scales "
+                        "rocprofv3's FETCH_SIZE / WRITE_SIZE counters)")
     return p.parse_args()
 
 
@@ -460,6 +463,16 @@ def main():
     if not torch.cuda.is_available() or not mx.device_supported():
         print("bench.py needs an MI355X (gfx950) GPU", file=sys.stderr)
         sys.exit(1)
+
+    if args.copy_calibration:
+        n = 1 << 30
+        src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            torch.add(src, 0.0, out=dst)    # reads 1 GiB, writes 1 GiB
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_calibration_bytes_read": n, "copy_calibration_bytes_written": n, "launches": 3}))
+        return
     if args.workload == "streamed":
         rec = bench_streamed(args)
     else:

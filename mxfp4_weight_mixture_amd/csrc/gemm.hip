@@ -445,8 +445,13 @@ __device__ __forceinline__ void wait_lgkm0() {
   __builtin_amdgcn_s_waitcnt(15 | (3 << 14) | (7 << 4));
 }
 
+// Workgroup barrier that also publishes this wave's LDS writes: s_barrier by
+// itself does not wait for outstanding LDS operations, so without the
+// lgkmcnt(0) another wave could read a location this wave's ds_write has not
+// reached yet (DMA writes are waited for separately, with vmcnt).
 __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
+  wait_lgkm0();
   __builtin_amdgcn_s_barrier();
   asm volatile("" ::: "memory");
 }

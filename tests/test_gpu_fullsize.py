@@ -76,3 +76,20 @@ def test_prefill256_full_size():
 
 def test_decode_t1_full_size():
     _full("decode", 1, 2e-2, T=1)
+
+
+def test_prefill896_repeat_runs_bitwise_identical():
+    """Five passes of the full-size layer (MXFP8 intermediate: FC1's epilogue
+    stages its fp32 tile through LDS between two barriers) agree bitwise: a
+    barrier that let a wave read the staged tile before another wave's LDS
+    writes had landed showed up here as an occasional garbage block."""
+    s = gen.preset("prefill896_mxfp8")
+    li = gen.layer_inputs(s)
+    w = device_weights(s)
+    layer = mx.Layer(*w, k=s.k, layout=s.layout, inter="mxfp8")
+    x, xs = device_x(li)
+    logits = torch.from_numpy(li.logits).to(DEV)
+    first = layer.forward(logits, x, xs).clone()
+    for _ in range(4):
+        assert torch.equal(layer.forward(logits, x, xs), first)
+    assert torch.isfinite(first).all()
