@@ -74,6 +74,7 @@ struct Params {
   uint8_t* c_scales;   // E8M0 [rows][n_out / 32], MXFP8 output only
   const Tile* tiles;
   const int32_t* tile_count;
+  int32_t* unit_ctr;          // [8] per-XCD unit counters of this launch (zeroed by the planner)
   int a_gather_div;
   int N, K, n_out, n_tiles;
   int layout;  // 0 none, 1 split, 2 interleaved
@@ -502,17 +503,27 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
   const int count = *p.tile_count;
   const int units = count * p.n_tiles;
   const int xcd = blockIdx.x % kXcds;
-  const int slot = blockIdx.x / kXcds;
-  const int slots = gridDim.x / kXcds;
   const int per_xcd = (units + kXcds - 1) / kXcds;
-  const int u_end = min(units, (xcd + 1) * per_xcd);
+  const int u_first = xcd * per_xcd;
+  const int u_end = min(units, u_first + per_xcd);
 
   const int K = p.K;
   const int a_row_bytes = FP8 ? K : 2 * K;
   const int kb = K / 32;
   const int nst = K / C::KS;
 
-  for (int u = xcd * per_xcd + slot; u < u_end; u += slots) {
+  // Units of an XCD's range are handed out dynamically (blocks whose units
+  // end early take more; blocks that start late take fewer).  Thread
+  // 0 draws the next index with an atomic one unit ahead; the index reaches
+  // the other threads through a slot in scale buffer 1, which is idle between
+  // units.
+  int* const unit_slot = reinterpret_cast<int*>(lds + C::NST * C::LDS_STAGE + C::LDS_SG);
+  if (threadIdx.x == 0) *unit_slot = atomicAdd(&p.unit_ctr[xcd], 1);
+  stage_barrier();
+  int u = u_first + *unit_slot;
+  while (u < u_end) {
+    int u_next = 0;
+    if (threadIdx.x == 0) u_next = atomicAdd(&p.unit_ctr[xcd], 1);
     // Lane-derived values are recomputed per unit from an opaque copy of the
     // thread index.  Hoisted out of the unit loop they stay live across it and
     // get spilled, and a spill reload in the pipeline prologue would wait for
@@ -601,6 +612,12 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
       for (int i = 0; i < C::B_I; ++i)
         dma16(rb, b_off[i], s * C::RB, base + C::LDS_A + (wave * C::B_I + i) * 1024);
     };
+    // DMA instruction j of stage s (j < A_I: A, then B), for interleaving with products
+    auto issue_one = [&](int s, int j) {
+      uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
+      if (j < C::A_I) dma16(ra, a_off[j], s * C::RA, base + (wave * C::A_I + j) * 1024);
+      else dma16(rb, b_off[j - C::A_I], s * C::RB, base + C::LDS_A + (wave * C::B_I + j - C::A_I) * 1024);
+    };
     // scale group j (stages 4j..4j+3): 16 bytes of every A and B row
     auto issue_scales = [&](int j) {
       uint8_t* base = sg + (j & 1) * C::LDS_SG;
@@ -666,12 +683,14 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
       // reads issued after each product: at least two (front-loaded), more for small tiles
       constexpr int R1 = (NR + MF - 1) / MF > 2 ? (NR + MF - 1) / MF : 2;
       constexpr int R2 = (NR + NS + MF - 1) / MF > 2 ? (NR + NS + MF - 1) / MF : 2;
-      // One stage.  ISSUE: refill the freed buffer with stage s+3 (SCALES: and the
-      // next scale group); WAIT: vmcnt allowance at the mid-stage barrier, -1 for
-      // the last stage (no barrier, no next-stage reads).  All three are compile-time
-      // constants so that the loop body has no branch the compiler could sink the
-      // first half's products past.  Every group of one product and its reads is
-      // fenced with sched_barrier to keep the interleave.
+      constexpr int D2 = (C::LOADS + MF - 1) / MF;   // refill DMA instructions per product
+      // One stage.  ISSUE: refill the freed buffer with stage s+3 during the second
+      // half (SCALES: and the next scale group); WAIT: vmcnt allowance at the
+      // mid-stage barrier, -1 for the last stage (no barrier, no next-stage
+      // reads).  All three are compile-time constants so that the loop body has
+      // no branch the compiler could sink the first half's products past.  Every
+      // group of one product and its reads / DMA is fenced with sched_barrier to
+      // keep the interleave.
       auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, const uint32_t (&ta)[C::FM],
                       const uint32_t (&tb)[C::FN], uint32_t (&tna)[C::FM], uint32_t (&tnb)[C::FN]) {
         constexpr bool kIssue = decltype(ISSUE)::value;
@@ -696,10 +715,6 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
           wait_lgkm0();
           wait_vm<kWait>();
           stage_barrier();
-          if constexpr (kIssue) {
-            issue(s + 3);
-            if constexpr (kScales) issue_scales((s + 3) >> 2);
-          }
         }
         __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
@@ -711,6 +726,14 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
             for (int r = R2 * i; r < R2 * i + R2; ++r) {
               if (r < NS) read_scale(s + 1, r, tna, tnb);
               else if (r < NS + NR) read_frag(s + 1, 0, r - NS, a0, b0);
+            }
+          }
+          // the refill of the freed buffer (stage s+3), spread over the products
+          if constexpr (kIssue) {
+#pragma unroll
+            for (int j = D2 * i; j < D2 * i + D2; ++j) {
+              if (j < C::LOADS) issue_one(s + 3, j);
+              if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
             }
           }
           __builtin_amdgcn_sched_barrier(0);
@@ -942,6 +965,9 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
     }
     // every wave is done with LDS before the next unit refills it
     stage_barrier();
+    if (threadIdx.x == 0) *unit_slot = u_next;
+    stage_barrier();
+    u = u_first + *unit_slot;
   }
 }
 
@@ -965,7 +991,8 @@ __device__ inline int4 wave_incl_scan4(int4 v) {
 // remainder goes to the smallest class of 32/64/128/256 rows that holds it.
 __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ offsets, int E,
                                                     int big_log2, Tile* __restrict__ lists, int cap,
-                                                    int32_t* __restrict__ counts) {
+                                                    int32_t* __restrict__ counts, int32_t* __restrict__ unit_ctr) {
+  if (threadIdx.x < kClasses * kXcds) unit_ctr[threadIdx.x] = 0;
   __shared__ int4 wave_tot[16];
   __shared__ int4 carry;
   const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
@@ -1034,31 +1061,45 @@ int persistent_grid(KernelT kernel) {
 }
 
 template <int BM, bool FP8, int EPI, int OUT, bool DMA>
-moe_status launch_class(const Params& p, hipStream_t s) {
+int class_grid() {
   static int grid = 0;  // per instantiation; one device type (gfx950)
-  if constexpr (DMA) {
-    if (grid == 0) grid = persistent_grid(gemm_dma_kernel<BM, FP8, EPI, OUT>);
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
-  } else {
-    if (grid == 0) grid = persistent_grid(gemm_kernel<BM, FP8, EPI, OUT>);
-    hipLaunchKernelGGL((gemm_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
+  if (grid == 0) {
+    if constexpr (DMA) grid = persistent_grid(gemm_dma_kernel<BM, FP8, EPI, OUT>);
+    else grid = persistent_grid(gemm_kernel<BM, FP8, EPI, OUT>);
   }
+  return grid;
+}
+
+template <int BM, bool FP8, int EPI, int OUT, bool DMA>
+moe_status launch_class(const Params& p, hipStream_t s) {
+  const int grid = class_grid<BM, FP8, EPI, OUT, DMA>();
+  if constexpr (DMA)
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
+  else
+    hipLaunchKernelGGL((gemm_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
   MXMOE_HIP(hipGetLastError());
   return MOE_OK;
 }
 
+// One launch per row-tile class, in order, on the caller's stream.  (Running
+// the HBM-bound small-tile classes beside the full-tile class on a slice of
+// the CUs was measured slower: a few CUs cannot pull the weight stream at
+// HBM rate, and the full tiles lose those CUs for longer.)
 template <bool FP8, int EPI, int OUT, bool DMA>
 moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* counts, hipStream_t s) {
-  p.tiles = lists + 0 * cap; p.tile_count = counts + 0;
-  MXMOE_TRY((launch_class<32, FP8, EPI, OUT, DMA>(p, s)));
-  p.tiles = lists + 1 * cap; p.tile_count = counts + 1;
-  MXMOE_TRY((launch_class<64, FP8, EPI, OUT, DMA>(p, s)));
-  p.tiles = lists + 2 * cap; p.tile_count = counts + 2;
-  MXMOE_TRY((launch_class<128, FP8, EPI, OUT, DMA>(p, s)));
-  // the bf16 DMA kernel's full tile is 128 rows, so its class-3 list is empty
+  int32_t* const ctr = p.unit_ctr;
+  auto at = [&](int c) {
+    p.tiles = lists + c * cap;
+    p.tile_count = counts + c;
+    p.unit_ctr = ctr + c * kXcds;
+  };
+  at(0); MXMOE_TRY((launch_class<32, FP8, EPI, OUT, DMA>(p, s)));
+  at(1); MXMOE_TRY((launch_class<64, FP8, EPI, OUT, DMA>(p, s)));
+  at(2); MXMOE_TRY((launch_class<128, FP8, EPI, OUT, DMA>(p, s)));
+  // the bf16 DMA kernel's full tile is 128 rows (its 256-row stages do not fit
+  // in LDS), so its class-3 list is empty
   if constexpr (!(DMA && !FP8)) {
-    p.tiles = lists + 3 * cap; p.tile_count = counts + 3;
-    MXMOE_TRY((launch_class<256, FP8, EPI, OUT, DMA>(p, s)));
+    at(3); MXMOE_TRY((launch_class<256, FP8, EPI, OUT, DMA>(p, s)));
   }
   return MOE_OK;
 }
@@ -1137,11 +1178,13 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
   const bool dma = a.K % 512 == 0;
   const bool fp8 = a.a_dtype == MOE_ACT_MXFP8_E4M3;
   const int big_log2 = (dma && !fp8) ? 7 : 8;
+  int32_t* unit_ctr = counts + 32;   // [class][xcd], inside the workspace's 256-byte count block
   hipLaunchKernelGGL(plan_kernel, dim3(1), dim3(1024), 0, s, a.expert_offsets, a.E, big_log2, lists, cap,
-                     counts);
+                     counts, unit_ctr);
   MXMOE_HIP(hipGetLastError());
 
   Params p{};
+  p.unit_ctr = unit_ctr;
   p.a = static_cast<const uint8_t*>(a.a);
   p.a_scales = a.a_scales;
   p.a_gather = a.a_gather;
