@@ -457,7 +457,10 @@ __device__ __forceinline__ void stage_barrier() {
   asm volatile("" ::: "memory");
 }
 
-__device__ __forceinline__ float silu_mul(float g, float u) { return g / (1.0f + __expf(-g)) * u; }
+// silu(g) * u with the hardware reciprocal (about 1 ulp) in place of an IEEE division
+__device__ __forceinline__ float silu_mul(float g, float u) {
+  return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
+}
 
 // fp32 -> E4M3 code, round to nearest even; |x| <= 448 or NaN (the MXFP8
 // scale below guarantees the bound).  Normal range: round the fp32
@@ -667,15 +670,26 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
         if (j < C::FM) ta[j] = *reinterpret_cast<const uint32_t*>(lsg + (wm0 + j * 32 + l32) * 16);
         else tb[j - C::FM] = *reinterpret_cast<const uint32_t*>(lsg + C::SG_A + (wn0 + (j - C::FM) * 32 + l32) * 16);
       };
-      // product i of one k-half, B-fragment major
+      // product i of one k-half, B-fragment major.  ta/tb hold this lane's scale
+      // bytes in the order the op_sel field reads them: byte kk = block 2kk + g.
       auto mma = [&](int kk, int i, const v8i (&af)[C::FM], const v4i (&bq)[C::FN], const uint32_t (&ta)[C::FM],
                      const uint32_t (&tb)[C::FN]) {
         const int fn = i / C::FM, fm = i % C::FM;
         const v8i bf = v8i{bq[fn][0], bq[fn][1], bq[fn][2], bq[fn][3], 0, 0, 0, 0};
-        const int bsc = (tb[fn] >> (8 * (2 * kk + g))) & 0xff;
-        const int asc = (ta[fm] >> (8 * (2 * kk + g))) & 0xff;
-        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0 /*A: fp8 e4m3*/,
-                                                                      4 /*B: fp4 e2m1*/, 0, asc, 0, bsc);
+        if (kk == 0)
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0 /*A: fp8 e4m3*/,
+                                                                        4 /*B: fp4 e2m1*/, 0, ta[fm], 0, tb[fn]);
+        else
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0, 4, 1, ta[fm],
+                                                                        1, tb[fn]);
+      };
+      // a stage's four scale bytes (blocks 0..3) -> this lane's two, in op_sel order
+      const uint32_t scale_sel = g ? 0x0c0c0301u : 0x0c0c0200u;
+      auto order_scales = [&](uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
+#pragma unroll
+        for (int j = 0; j < C::FM; ++j) ta[j] = __builtin_amdgcn_perm(0u, ta[j], scale_sel);
+#pragma unroll
+        for (int j = 0; j < C::FN; ++j) tb[j] = __builtin_amdgcn_perm(0u, tb[j], scale_sel);
       };
       constexpr int MF = C::FM * C::FN;
       constexpr int NR = 2 * C::FM + C::FN;   // fragment reads of one k-half
@@ -691,11 +705,12 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
       // no branch the compiler could sink the first half's products past.  Every
       // group of one product and its reads / DMA is fenced with sched_barrier to
       // keep the interleave.
-      auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, const uint32_t (&ta)[C::FM],
-                      const uint32_t (&tb)[C::FN], uint32_t (&tna)[C::FM], uint32_t (&tnb)[C::FN]) {
+      auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN],
+                      uint32_t (&tna)[C::FM], uint32_t (&tnb)[C::FN]) {
         constexpr bool kIssue = decltype(ISSUE)::value;
         constexpr bool kScales = decltype(SCALES)::value;
         constexpr int kWait = decltype(WAIT)::value;
+        order_scales(ta, tb);
 #pragma unroll
         for (int i = 0; i < MF; ++i) {
           mma(0, i, a0, b0, ta, tb);
