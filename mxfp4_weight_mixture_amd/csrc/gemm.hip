@@ -387,10 +387,18 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
 // 16 different 16-byte bank groups, and any 8 consecutive rows 8 different
 // ones, with no padding.
 
-template <int BM, bool FP8>
+// Waves per block.  The full FP8 tile of FC1 runs eight (two per SIMD, each
+// wave a 64x128 slice): measured faster than four 128x128 waves for FC1.
+// FC2's (bf16 output staged through LDS) spills at eight and stays at four.
+template <int BM, bool FP8, int EPI>
+constexpr int dma_waves() { return (BM == 256 && FP8 && EPI != 0) ? 8 : 4; }
+
+template <int BM, bool FP8, int NWAVES = 4>
 struct Cfg2 {
-  static constexpr int WAVES_M = BM >= 128 ? 2 : 1;
-  static constexpr int WAVES_N = 4 / WAVES_M;
+  static constexpr int NW = NWAVES;
+  static constexpr int NT = NW * 64;
+  static constexpr int WAVES_M = NW == 8 ? 4 : (BM >= 128 ? 2 : 1);
+  static constexpr int WAVES_N = NW / WAVES_M;
   static constexpr int WM = BM / WAVES_M;
   static constexpr int WN = kBN / WAVES_N;
   static constexpr int FM = WM / 32;
@@ -407,8 +415,8 @@ struct Cfg2 {
   static constexpr int SG_B = kBN * 16;
   static constexpr int LDS_SG = SG_A + SG_B;
   static constexpr int LDS_TOTAL = NST * LDS_STAGE + 2 * LDS_SG;
-  static constexpr int A_I = BM * RA / 4096;        // A DMA instructions per wave per stage
-  static constexpr int B_I = kBN * RB / 4096;       // B DMA instructions per wave per stage (4)
+  static constexpr int A_I = BM * RA / (NW * 1024);  // A DMA instructions per wave per stage
+  static constexpr int B_I = kBN * RB / (NW * 1024);  // B DMA instructions per wave per stage
   static constexpr int A_ROWS_PER_I = 1024 / RA;    // A rows one instruction fills
   static constexpr int LOADS = A_I + B_I;           // data DMA instructions per wave per stage
   static_assert(LDS_TOTAL <= 163840, "LDS budget");
@@ -499,8 +507,8 @@ __device__ inline int mxfp8_block_exp(float amax) {
 // frees stage s's buffer for the DMA of stage s+3.  bf16 operands: the
 // stage's reads and products follow one barrier at its start.
 template <int BM, bool FP8, int EPI, int OUT>
-__global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
-  using C = Cfg2<BM, FP8>;
+__global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_kernel(Params p) {
+  using C = Cfg2<BM, FP8, dma_waves<BM, FP8, EPI>()>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_TOTAL];
 
   const int count = *p.tile_count;
@@ -592,10 +600,15 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
       const int wr = w_row_of<C::WN>(p.layout, nt, j, p.N, p.n_out);
       b_off[i] = (uint32_t)wr * (uint32_t)(K / 2) + (uu & 3) * 16;
     }
-    const int srow = wave * 64 + lane;   // scale row this lane loads (A: if < BM)
+    // scale loads: with four waves every wave loads 64 rows of A scales (if
+    // below BM) and 64 of B scales; with eight, waves 0-3 load A, 4-7 load B
+    const bool a_sw = C::NW == 8 ? wave < 4 : true;
+    const bool b_sw = C::NW == 8 ? wave >= 4 : true;
+    const int sw = (C::NW == 8 && wave >= 4) ? wave - 4 : wave;
+    const int srow = sw * 64 + lane;   // scale row this lane loads (A: if < BM)
     const uint8_t* const as_base = gather ? p.a_scales : p.a_scales + (size_t)row0 * kb;
     uint32_t as_off = 0;
-    if (FP8 && srow < BM) {
+    if (FP8 && a_sw && srow < BM) {
       const int r = min(srow, mrows - 1);
       as_off = (uint32_t)(gather ? p.a_gather[row0 + r] / p.a_gather_div : r) * (uint32_t)kb;
     }
@@ -624,8 +637,8 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
     // scale group j (stages 4j..4j+3): 16 bytes of every A and B row
     auto issue_scales = [&](int j) {
       uint8_t* base = sg + (j & 1) * C::LDS_SG;
-      if (FP8 && wave * 64 < BM) dma16(ras, as_off, 16 * j, base + wave * 1024);
-      dma16(rbs, bs_off, 16 * j, base + C::SG_A + wave * 1024);
+      if (FP8 && a_sw && sw * 64 < BM) dma16(ras, as_off, 16 * j, base + sw * 1024);
+      if (b_sw) dma16(rbs, bs_off, 16 * j, base + C::SG_A + sw * 1024);
     };
 
     v16f acc[C::FM][C::FN];
@@ -923,7 +936,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
         const bool vec = ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && (ld % 8 == 0);
         constexpr int CPR = TC / 8;   // 16-byte chunks per tile row
         uint16_t* const out = static_cast<uint16_t*>(p.c) + (size_t)row0 * ld + col0;
-        for (int idx = tid; idx < mrows * CPR; idx += kThreads) {
+        for (int idx = tid; idx < mrows * CPR; idx += C::NT) {
           const int r = idx / CPR, c = (idx % CPR) * 8;
           if (c >= ncols) continue;
           const uint4 v = *reinterpret_cast<const uint4*>(lds + r * PITCH + c * 2);
@@ -944,7 +957,7 @@ __global__ __launch_bounds__(kThreads) void gemm_dma_kernel(Params p) {
         constexpr int BPR = TC / 32;   // blocks per tile row
         uint8_t* const out = static_cast<uint8_t*>(p.c) + (size_t)row0 * ld + col0;
         uint8_t* const osc = p.c_scales + (size_t)row0 * (ld / 32) + col0 / 32;
-        for (int idx = tid; idx < mrows * BPR; idx += kThreads) {
+        for (int idx = tid; idx < mrows * BPR; idx += C::NT) {
           const int r = idx / BPR, c = (idx % BPR) * 32;
           if (c >= ncols) continue;
           const float4* src = reinterpret_cast<const float4*>(lds + r * PITCH + c * 4);
@@ -1067,9 +1080,9 @@ __global__ __launch_bounds__(1024) void plan_kernel(const int32_t* __restrict__ 
 int list_capacity(int rows, int E) { return rows / 32 + E + 8; }  // >= rows/128 + E per class
 
 template <typename KernelT>
-int persistent_grid(KernelT kernel) {
+int persistent_grid(KernelT kernel, int threads = kThreads) {
   int per_cu = 0;
-  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, kThreads, 0) != hipSuccess || per_cu < 1)
+  if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, threads, 0) != hipSuccess || per_cu < 1)
     per_cu = 1;
   const int grid = num_cus() * per_cu;
   return (grid + kXcds - 1) / kXcds * kXcds;
@@ -1079,7 +1092,7 @@ template <int BM, bool FP8, int EPI, int OUT, bool DMA>
 int class_grid() {
   static int grid = 0;  // per instantiation; one device type (gfx950)
   if (grid == 0) {
-    if constexpr (DMA) grid = persistent_grid(gemm_dma_kernel<BM, FP8, EPI, OUT>);
+    if constexpr (DMA) grid = persistent_grid(gemm_dma_kernel<BM, FP8, EPI, OUT>, 64 * dma_waves<BM, FP8, EPI>());
     else grid = persistent_grid(gemm_kernel<BM, FP8, EPI, OUT>);
   }
   return grid;
@@ -1089,7 +1102,8 @@ template <int BM, bool FP8, int EPI, int OUT, bool DMA>
 moe_status launch_class(const Params& p, hipStream_t s) {
   const int grid = class_grid<BM, FP8, EPI, OUT, DMA>();
   if constexpr (DMA)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(64 * dma_waves<BM, FP8, EPI>()), 0,
+                       s, p);
   else
     hipLaunchKernelGGL((gemm_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
   MXMOE_HIP(hipGetLastError());
