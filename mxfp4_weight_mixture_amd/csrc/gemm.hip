@@ -470,22 +470,16 @@ __device__ __forceinline__ float silu_mul(float g, float u) {
   return g * __builtin_amdgcn_rcpf(1.0f + __expf(-g)) * u;
 }
 
-// fp32 -> E4M3 code, round to nearest even; |x| <= 448 or NaN (the MXFP8
-// scale below guarantees the bound).  Normal range: round the fp32
-// significand to 3 bits in integer arithmetic; below 2^-6: multiples of 2^-9.
-__device__ inline uint32_t e4m3_rne(float x) {
-  const uint32_t sign = (__float_as_uint(x) >> 24) & 0x80u;
-  const float a = fabsf(x);
-  if (a != a) return 0x7fu;
-  uint32_t code;
-  if (a < 0.015625f) {
-    code = (uint32_t)__builtin_rintf(a * 512.0f);   // 0..8 (8 = smallest normal)
-  } else {
-    const uint32_t b = __float_as_uint(a);
-    const uint32_t r = b + 0x7ffffu + ((b >> 20) & 1u);
-    code = (r >> 20) - (120u << 3);
-  }
-  return sign | code;
+// Four fp32 values (|x| <= 448, which the MXFP8 scale below guarantees) ->
+// four E4M3 codes, little-endian in one word, round to nearest even with
+// E4M3 subnormals: the packed scaled conversion with scale 1.0.
+typedef short short2_t __attribute__((ext_vector_type(2)));
+__device__ inline uint32_t e4m3x4_rne(float a, float b, float c, float d) {
+  const short2_t z = {0, 0};
+  const short2_t lo = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, a, b, 1.0f, false);
+  const short2_t hi = __builtin_amdgcn_cvt_scalef32_pk_fp8_f32(z, c, d, 1.0f, false);
+  // each result holds its two codes in the low half-word (first value in byte 0)
+  return (uint32_t)(uint16_t)lo.x | ((uint32_t)(uint16_t)hi.x << 16);
 }
 
 // E8M0 exponent X of one MXFP8 block: the smallest X with amax * 2^-X <= 448
@@ -972,7 +966,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
               const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              *reinterpret_cast<uint16_t*>(col + r * PITCH) = (uint16_t)bf16_rne(acc[fm][fn][q]);
+              *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)acc[fm][fn][q];   // v_cvt_pk_bf16_f32 (RNE)
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -987,7 +981,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
               const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
               const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
               if constexpr (MX) *reinterpret_cast<float*>(col + r * PITCH) = a;
-              else *reinterpret_cast<uint16_t*>(col + r * PITCH) = (uint16_t)bf16_rne(a);
+              else *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)a;
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -1037,12 +1031,9 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
           const int x = mxfp8_block_exp(amax);
           uint32_t w[8];
 #pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            uint32_t q = 0;
-#pragma unroll
-            for (int t = 0; t < 4; ++t) q |= e4m3_rne(ldexpf(v[4 * j + t], -x)) << (8 * t);
-            w[j] = q;
-          }
+          for (int j = 0; j < 8; ++j)
+            w[j] = e4m3x4_rne(ldexpf(v[4 * j], -x), ldexpf(v[4 * j + 1], -x),
+                              ldexpf(v[4 * j + 2], -x), ldexpf(v[4 * j + 3], -x));
           uint8_t* dst = out + (size_t)r * ld + c;
           if (vec) {
             reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
