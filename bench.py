@@ -293,6 +293,11 @@ def bench_layer(args):
     ms = float(split.sum())
     log(f"[bench] per step ms: " + ", ".join(f"{n} {v:.3f}" for n, v in zip(Steps.NAMES, split)))
 
+    graph = None
+    if name in ("decode", "tiny"):
+        graph = bench_graph(shape, w, x, xs, logits, inter, args)
+        log(f"[bench] graph replay {graph['replay_ms']:.4f} ms vs eager layer call {graph['eager_forward_ms']:.4f} ms")
+
     T, H, I, k, E = shape.T, shape.H, shape.I, shape.k, shape.E
     rows = T * k
     flops = gen.flops(shape)
@@ -348,7 +353,41 @@ def bench_layer(args):
         "roofline": roof,
         "checks": parity,
     }
+    if graph is not None:
+        rec["graph"] = graph
     return rec, shape, li, ids
+
+
+def bench_graph(shape, w, x, xs, logits, inter, args):
+    """The resident layer as one eager moe_layer_forward call vs one replay of its
+    captured graph (moe_layer_graph_*), each timed over the same step count; the
+    replay must equal the eager output bitwise."""
+    layer = mx.Layer(*w, k=shape.k, layout=shape.layout, inter=inter)
+    eager = layer.forward(logits, x, xs).clone()
+    g = layer.capture(logits, x, xs)
+    try:
+        torch.cuda.synchronize()
+        same = bool(torch.equal(g.replay(), eager))
+        torch.cuda.synchronize()
+
+        def timed(fn):
+            for _ in range(args.warmup):
+                fn()
+            a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            a.record()
+            for _ in range(args.steps):
+                fn()
+            b.record()
+            torch.cuda.synchronize()
+            return a.elapsed_time(b) / args.steps
+
+        eager_ms = timed(lambda: layer.forward(logits, x, xs))
+        replay_ms = timed(g.replay)
+    finally:
+        g.close()
+    return {"replay_ms": replay_ms, "eager_forward_ms": eager_ms, "replay_equals_eager": same,
+            "note": "back-to-back steps on one stream, no per-step sync"}
 
 
 def bench_streamed(args):

@@ -241,6 +241,38 @@ size_t     moe_layer_workspace_offset(int32_t T, int32_t H, int32_t I, int32_t E
 /* route -> permute -> FC1 + SwiGLU -> FC2 -> combine, all on `stream`. */
 moe_status moe_layer_forward(const moe_layer_args* args, void* stream);
 
+/* ------------------------------------------------ captured layer ------ */
+
+/* Graph capture and replay of one resident layer ("Kimi-K3 SM120 FlashInfer
+ * MXFP4 MoE" page, Phase-1 gates, item 5: token counts 1/2/8/32 under graph
+ * capture/replay).
+ *
+ * moe_layer_graph_create validates *args exactly as moe_layer_forward does,
+ * captures one moe_layer_forward(args) on `stream` into a HIP graph and
+ * instantiates it.  Nothing runs during the capture.  The graph keeps every
+ * pointer of *args (not the struct itself): a replay reads the inputs'
+ * contents at replay time and writes the same outputs and workspace, so
+ * replays on one handle must not overlap each other or a moe_layer_forward
+ * on the same workspace.  T, the weights and the workspace are fixed per
+ * handle.  `stream` must be a created stream (capture on the null stream
+ * is MOE_ERR_INVALID_ARG) with no other capture in progress; it is left in
+ * normal (non-capturing) mode on every return.  On failure *graph is NULL
+ * and the status is forward's (or MOE_ERR_HIP for a capture/instantiate
+ * failure).  The handle is host memory owned by the caller until
+ * moe_layer_graph_destroy.
+ *
+ * moe_layer_graph_launch enqueues one replay on `stream` (any stream of the
+ * device the graph was captured on; MOE_ERR_INVALID_ARG on another device).
+ * Output ordering is that of a kernel launch on `stream`.
+ *
+ * moe_layer_graph_destroy frees the handle (NULL is accepted); the caller
+ * first makes sure no replay is still running.
+ */
+typedef struct moe_layer_graph moe_layer_graph;
+moe_status moe_layer_graph_create(const moe_layer_args* args, void* stream, moe_layer_graph** graph);
+moe_status moe_layer_graph_launch(moe_layer_graph* graph, void* stream);
+moe_status moe_layer_graph_destroy(moe_layer_graph* graph);
+
 /* ------------------------------------------------ streamed prefill ---- */
 
 typedef struct moe_streamed_args {

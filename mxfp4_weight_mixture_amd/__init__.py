@@ -85,6 +85,9 @@ def _load():
         "moe_blob_section_offset": (_sz, [_i32, _i32, _i32, _i32]),
         "moe_streamed_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
         "moe_layer_prefill_streamed": (ctypes.c_int, [ctypes.POINTER(StreamedArgs), _vp, _vp]),
+        "moe_layer_graph_create": (ctypes.c_int, [ctypes.POINTER(LayerArgs), _vp, ctypes.POINTER(_vp)]),
+        "moe_layer_graph_launch": (ctypes.c_int, [_vp, _vp]),
+        "moe_layer_graph_destroy": (ctypes.c_int, [_vp]),
     }
     for name, (res, args) in sigs.items():
         fn = getattr(lib, name)
@@ -218,6 +221,16 @@ class Layer:
     def workspace_bytes(self, T: int) -> int:
         return lib.moe_layer_workspace_size(T, self.H, self.I, self.E, self.k, self.inter)
 
+    def _args(self, T, logits, x, x_scales, out, x_next, ws):
+        return LayerArgs(T=T, H=self.H, I=self.I, E=self.E, k=self.k, layout=self.layout,
+                         act_dtype=1 if x_scales is not None else 0, inter_dtype=self.inter,
+                         logits=logits.data_ptr(), x=x.data_ptr(),
+                         x_scales=x_scales.data_ptr() if x_scales is not None else None,
+                         w1_packed=self.w1p.data_ptr(), w1_scales=self.w1s.data_ptr(),
+                         w2_packed=self.w2p.data_ptr(), w2_scales=self.w2s.data_ptr(), out=out.data_ptr(),
+                         x_next=x_next.data_ptr() if x_next is not None else None,
+                         workspace=ws.data_ptr(), workspace_bytes=ws.numel())
+
     def forward(self, logits: torch.Tensor, x: torch.Tensor, x_scales: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, x_next: Optional[torch.Tensor] = None, stream=None):
         T = logits.shape[0]
@@ -226,16 +239,14 @@ class Layer:
             self._ws = _u8(n, logits.device)
         if out is None:
             out = torch.empty((T, self.H), dtype=torch.float32, device=logits.device)
-        args = LayerArgs(T=T, H=self.H, I=self.I, E=self.E, k=self.k, layout=self.layout,
-                         act_dtype=1 if x_scales is not None else 0, inter_dtype=self.inter,
-                         logits=logits.data_ptr(), x=x.data_ptr(),
-                         x_scales=x_scales.data_ptr() if x_scales is not None else None,
-                         w1_packed=self.w1p.data_ptr(), w1_scales=self.w1s.data_ptr(),
-                         w2_packed=self.w2p.data_ptr(), w2_scales=self.w2s.data_ptr(), out=out.data_ptr(),
-                         x_next=x_next.data_ptr() if x_next is not None else None,
-                         workspace=self._ws.data_ptr(), workspace_bytes=self._ws.numel())
+        args = self._args(T, logits, x, x_scales, out, x_next, self._ws)
         _check(lib.moe_layer_forward(ctypes.byref(args), _stream(stream)))
         return out
+
+    def capture(self, logits: torch.Tensor, x: torch.Tensor, x_scales: Optional[torch.Tensor] = None,
+                out: Optional[torch.Tensor] = None, x_next: Optional[torch.Tensor] = None) -> "LayerGraph":
+        """moe_layer_graph_create: this layer on these buffers, captured once; see LayerGraph."""
+        return LayerGraph(self, logits, x, x_scales, out, x_next)
 
     def routing(self, T: int):
         """Views of the routing arrays the last forward() wrote into its workspace."""
@@ -246,6 +257,60 @@ class Layer:
         return dict(ids=view(0, Tk, torch.int32).view(T, self.k), w=view(1, Tk, torch.float32).view(T, self.k),
                     offsets=view(2, self.E + 1, torch.int32), perm_src=view(3, Tk, torch.int32),
                     dest_row=view(4, Tk, torch.int32))
+
+
+class LayerGraph:
+    """A resident layer captured into a HIP graph (moe_layer_graph_*).
+
+    The graph owns its workspace and keeps the tensors it was captured on:
+    replay() runs the five steps with one launch, reading the current contents
+    of logits / x / x_scales and writing `out` (and x_next).  Replays on one
+    graph must not overlap each other.
+    """
+
+    def __init__(self, layer: Layer, logits, x, x_scales=None, out=None, x_next=None):
+        T = logits.shape[0]
+        dev = logits.device
+        self.layer, self.T = layer, T
+        self.logits, self.x, self.x_scales, self.x_next = logits, x, x_scales, x_next
+        self.out = out if out is not None else torch.empty((T, layer.H), dtype=torch.float32, device=dev)
+        self.ws = _u8(layer.workspace_bytes(T), dev)
+        args = layer._args(T, logits, x, x_scales, self.out, x_next, self.ws)
+        # capture needs a created stream; nothing runs during the capture
+        side = torch.cuda.Stream(device=dev)
+        self._h = ctypes.c_void_p()
+        _check(lib.moe_layer_graph_create(ctypes.byref(args), ctypes.c_void_p(side.cuda_stream),
+                                          ctypes.byref(self._h)))
+
+    def replay(self, stream=None) -> torch.Tensor:
+        if not self._h:
+            raise MoeError(STATUS["MOE_ERR_INVALID_ARG"], "graph already destroyed")
+        _check(lib.moe_layer_graph_launch(self._h, _stream(stream)))
+        return self.out
+
+    def routing(self):
+        """Views of the routing arrays the last replay wrote into the graph's workspace."""
+        L = self.layer
+        def view(which, count, dtype):
+            off = lib.moe_layer_workspace_offset(self.T, L.H, L.I, L.E, L.k, L.inter, which)
+            return self.ws[off: off + 4 * count].view(dtype)
+        Tk = self.T * L.k
+        return dict(ids=view(0, Tk, torch.int32).view(self.T, L.k), w=view(1, Tk, torch.float32).view(self.T, L.k),
+                    offsets=view(2, L.E + 1, torch.int32), perm_src=view(3, Tk, torch.int32),
+                    dest_row=view(4, Tk, torch.int32))
+
+    def close(self):
+        """moe_layer_graph_destroy; waits for the device first so that no replay is still running."""
+        if self._h:
+            torch.cuda.synchronize(self.out.device)
+            h, self._h = self._h, ctypes.c_void_p()
+            _check(lib.moe_layer_graph_destroy(h))
+
+    def __del__(self):
+        try:
+            self.close()
+        except Exception:
+            pass
 
 
 def blob_bytes(H: int, I: int, E: int) -> int:

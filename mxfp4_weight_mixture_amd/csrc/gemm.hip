@@ -631,7 +631,8 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
     // scale group j (stages 4j..4j+3): 16 bytes of every A and B row
     auto issue_scales = [&](int j) {
       uint8_t* base = sg + (j & 1) * C::LDS_SG;
-      if (FP8 && a_sw && sw * 64 < BM) dma16(ras, as_off, 16 * j, base + sw * 1024);
+      // (a 32-row tile has 512 bytes of A scales per group: lanes 32-63 stay idle)
+      if (FP8 && a_sw && sw * 64 < BM && (BM >= 64 || lane < BM)) dma16(ras, as_off, 16 * j, base + sw * 1024);
       if (b_sw) dma16(rbs, bs_off, 16 * j, base + C::SG_A + sw * 1024);
     };
 

@@ -123,3 +123,19 @@ def test_blob_layout_sections_are_aligned_and_ordered():
     total = mx.blob_bytes(H, I, E)
     # 3*H*I weights per expert at 4 bits + one scale byte per 32: ~3.42 GB per layer
     assert total == E * 3 * H * I * 17 // 32
+
+
+def test_layer_graph_argument_errors():
+    """Graph capture rejects a missing handle, missing args and the null stream
+    before any device call; destroying NULL is a no-op, launching it an error."""
+    args = mx.LayerArgs(T=4, H=128, I=64, E=4, k=2, layout=1, act_dtype=0, inter_dtype=1)
+    h = ctypes.c_void_p()
+    st, msg = _status(mx.lib.moe_layer_graph_create(ctypes.byref(args), None, ctypes.byref(h)))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "null stream" in msg and not h.value
+    st, msg = _status(mx.lib.moe_layer_graph_create(ctypes.byref(args), ctypes.c_void_p(16), None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "handle" in msg
+    st, msg = _status(mx.lib.moe_layer_graph_create(None, ctypes.c_void_p(16), ctypes.byref(h)))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "null args" in msg
+    assert mx.lib.moe_layer_graph_destroy(None) == 0
+    st, msg = _status(mx.lib.moe_layer_graph_launch(None, None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "handle" in msg
