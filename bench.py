@@ -20,6 +20,7 @@ oracle runs here only in the CPU-baseline leg.
 from __future__ import annotations
 
 import argparse
+import hashlib
 import json
 import math
 import os
@@ -328,6 +329,7 @@ def bench_layer(args):
                 "traffic": None, "kernel": f"{dom} grouped GEMM", "per_launch_ms": dm,
                 "algorithmic_per_launch": dfl}
     roof["frac"] = roof["achieved"] / roof["peak"]
+    roof["traffic"] = measured_traffic(name, inter, dom)
     rec = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -356,6 +358,22 @@ def bench_layer(args):
     if graph is not None:
         rec["graph"] = graph
     return rec, shape, li, ids
+
+
+def measured_traffic(workload, inter, call):
+    """HBM bytes (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration)
+    of one `call` ("fc1"/"fc2"), as the rocprofv3 counter runs under profiles/
+    recorded them, or None when there is no record for this workload or the
+    grouped-GEMM source has changed since it was taken."""
+    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    rec = json.load(open(path))
+    src = os.path.join(ROOT, "mxfp4_weight_mixture_amd", "csrc", "gemm.hip")
+    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
+    if rec.get("gemm_source_sha256") != sha or rec.get("intermediate_dtype") != inter:
+        return None
+    return rec.get(f"{call}_bytes")
 
 
 def bench_graph(shape, w, x, xs, logits, inter, args):
