@@ -60,6 +60,9 @@ def parse():
     p.add_argument("--inter", default=None, choices=["bf16", "mxfp8"],
                    help="precision of the SwiGLU output fed to FC2 (default: mxfp8 for MXFP8 "
                         "activations with hidden % 512 == 0, else bf16)")
+    p.add_argument("--w-format", default=None, choices=["canonical", "tiled"],
+                   help="weight order the GEMMs read (default: tiled at load time, untimed, when hidden "
+                        "and intermediate are multiples of 512, else canonical)")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true", help="skip the output checks (profiling runs)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -74,7 +77,7 @@ class Steps:
     """The five ABI calls of one layer, with events between them on one stream."""
     NAMES = ["route", "permute", "fc1", "fc2", "combine"]
 
-    def __init__(self, shape, w, x, xs, logits, inter="bf16"):
+    def __init__(self, shape, w, x, xs, logits, inter="bf16", w_format="canonical"):
         self.s = shape
         self.inter = inter
         self.w1p, self.w1s, self.w2p, self.w2s = w
@@ -100,12 +103,13 @@ class Steps:
                               w_scales=self.w1s.data_ptr(), expert_offsets=self.off.data_ptr(),
                               c=self.act.data_ptr(), c_scales=self.act_s.data_ptr() if mx8 else None,
                               a_dtype=1 if xs is not None else 0, a_gather_div=k, a_rows=T, rows=rows, E=E,
-                              N=2 * I, K=H, epilogue=lay, c_dtype=2 if mx8 else 1)
+                              N=2 * I, K=H, epilogue=lay, c_dtype=2 if mx8 else 1,
+                              w_format=mx.W_FORMAT[w_format])
         self.g2 = mx.GemmArgs(a=self.act.data_ptr(), a_scales=self.act_s.data_ptr() if mx8 else None,
                               a_gather=None, w_packed=self.w2p.data_ptr(), w_scales=self.w2s.data_ptr(),
                               expert_offsets=self.off.data_ptr(), c=self.y.data_ptr(), c_scales=None,
                               a_dtype=1 if mx8 else 0, a_gather_div=1, a_rows=rows, rows=rows, E=E, N=H, K=I,
-                              epilogue=0, c_dtype=1)
+                              epilogue=0, c_dtype=1, w_format=mx.W_FORMAT[w_format])
         import ctypes
         self.ctypes = ctypes
         n = max(mx.lib.moe_grouped_gemm_workspace_size(ctypes.byref(self.g1)),
@@ -267,7 +271,17 @@ def bench_layer(args):
     log(f"[bench] {name}: inputs ready in {time.time() - t0:.1f}s")
 
     inter = args.inter or ("mxfp8" if shape.act == "mxfp8" and shape.H % 512 == 0 else "bf16")
-    steps = Steps(shape, w, x, xs, logits, inter)
+    w_format = args.w_format or ("tiled" if shape.H % 512 == 0 and shape.I % 512 == 0 else "canonical")
+    if w_format == "tiled":
+        # load-time reorder of both weight matrices (one resident copy), not timed
+        t1 = mx.tile_weights(w[0], w[1], shape.layout)
+        t2 = mx.tile_weights(w[2], w[3], "none")
+        w = (*t1, *t2)
+        del t1, t2
+        torch.cuda.synchronize()
+        torch.cuda.empty_cache()
+        log(f"[bench] weights tiled at load in {time.time() - t0:.1f}s (cumulative)")
+    steps = Steps(shape, w, x, xs, logits, inter, w_format)
     steps.run()
     torch.cuda.synchronize()
     ids = steps.ids.cpu().numpy()
@@ -296,7 +310,7 @@ def bench_layer(args):
 
     graph = None
     if name in ("decode", "tiny"):
-        graph = bench_graph(shape, w, x, xs, logits, inter, args)
+        graph = bench_graph(shape, w, x, xs, logits, inter, args, w_format)
         log(f"[bench] graph replay {graph['replay_ms']:.4f} ms vs eager layer call {graph['eager_forward_ms']:.4f} ms")
 
     T, H, I, k, E = shape.T, shape.H, shape.I, shape.k, shape.E
@@ -329,7 +343,7 @@ def bench_layer(args):
                 "traffic": None, "kernel": f"{dom} grouped GEMM", "per_launch_ms": dm,
                 "algorithmic_per_launch": dfl}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(name, inter, dom)
+    roof["traffic"] = measured_traffic(name, inter, dom, w_format)
     rec = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -345,6 +359,7 @@ def bench_layer(args):
         "data": "synthetic",
         "config": {"workload": name, "T": T, "hidden": H, "intermediate": I, "experts": E, "top_k": k,
                    "activations": shape.act, "intermediate_dtype": inter, "gate_up": shape.layout,
+                   "weight_format": w_format,
                    "router_bias": shape.bias,
                    "experts_hit": n_hit, "parallelism": "none (1 GPU)"},
         "tflops": tflops,
@@ -360,7 +375,7 @@ def bench_layer(args):
     return rec, shape, li, ids
 
 
-def measured_traffic(workload, inter, call):
+def measured_traffic(workload, inter, call, w_format):
     """HBM bytes (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration)
     of one `call` ("fc1"/"fc2"), as the rocprofv3 counter runs under profiles/
     recorded them, or None when there is no record for this workload or the
@@ -371,16 +386,17 @@ def measured_traffic(workload, inter, call):
     rec = json.load(open(path))
     src = os.path.join(ROOT, "mxfp4_weight_mixture_amd", "csrc", "gemm.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("gemm_source_sha256") != sha or rec.get("intermediate_dtype") != inter:
+    if rec.get("gemm_source_sha256") != sha or rec.get("intermediate_dtype") != inter \
+            or rec.get("weight_format", "canonical") != w_format:
         return None
     return rec.get(f"{call}_bytes")
 
 
-def bench_graph(shape, w, x, xs, logits, inter, args):
+def bench_graph(shape, w, x, xs, logits, inter, args, w_format="canonical"):
     """The resident layer as one eager moe_layer_forward call vs one replay of its
     captured graph (moe_layer_graph_*), each timed over the same step count; the
     replay must equal the eager output bitwise."""
-    layer = mx.Layer(*w, k=shape.k, layout=shape.layout, inter=inter)
+    layer = mx.Layer(*w, k=shape.k, layout=shape.layout, inter=inter, w_format=w_format)
     eager = layer.forward(logits, x, xs).clone()
     g = layer.capture(logits, x, xs)
     try:

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MXMOE_ABI_VERSION 1
+#define MXMOE_ABI_VERSION 2
 
 /* Every enum value is explicit and checked by the binding at load time:
  * a value that means one thing on one side of the boundary and another on
@@ -89,8 +89,14 @@ typedef enum moe_chain {         /* how stacked layers feed each other */
   MOE_CHAIN_INDEPENDENT = 1      /* every layer reads x_0 */
 } moe_chain;
 
+typedef enum moe_weight_format { /* how a weight matrix and its scales sit in memory */
+  MOE_W_CANONICAL = 0,           /* packed [E][N][K/2], scales [E][N][K/32] (row-major) */
+  MOE_W_TILED = 1                /* the load-time tiling of moe_mxfp4_tile_weights */
+} moe_weight_format;
+
 typedef enum moe_enum_kind {
-  MOE_ENUM_STATUS = 0, MOE_ENUM_ACT = 1, MOE_ENUM_OUT = 2, MOE_ENUM_EPI = 3, MOE_ENUM_CHAIN = 4
+  MOE_ENUM_STATUS = 0, MOE_ENUM_ACT = 1, MOE_ENUM_OUT = 2, MOE_ENUM_EPI = 3, MOE_ENUM_CHAIN = 4,
+  MOE_ENUM_WFORMAT = 5
 } moe_enum_kind;
 
 /* ------------------------------------------------------------ queries -- */
@@ -164,6 +170,9 @@ typedef struct moe_gemm_args {
   int32_t        E, N, K;
   int32_t        epilogue;       /* moe_epilogue */
   int32_t        c_dtype;        /* moe_out_dtype (MXFP8 only with a SWIGLU epilogue) */
+  int32_t        w_format;       /* moe_weight_format of w_packed / w_scales; MOE_W_TILED
+                                    needs K % 512 == 0 and N % 256 == 0 and weights tiled
+                                    with this call's epilogue */
 } moe_gemm_args;
 
 size_t     moe_grouped_gemm_workspace_size(const moe_gemm_args* args);
@@ -189,6 +198,38 @@ size_t     moe_grouped_gemm_workspace_size(const moe_gemm_args* args);
  */
 moe_status moe_mxfp4_grouped_gemm(const moe_gemm_args* args, void* workspace,
                                   size_t workspace_bytes, void* stream);
+
+/* ----------------------------------------------- load-time weight tiling -- */
+
+/* Load-time repacking of one weight matrix into the order the grouped GEMM
+ * streams it: the counterpart of the MXFP4 weight repack and E8M0 scale
+ * swizzle that ktransformers issue #2172 (comments on the Marlin MoE path)
+ * describes, where raw and repacked copies were both kept; here the caller
+ * frees the canonical copy once the tiled one is made.  A 256-column slice of the
+ * GEMM ("n-tile") over 128 K elements is one contiguous 16 KB block, already
+ * in the slot order the kernels read from LDS, so every weight load is 1 KB
+ * of consecutive bytes; an n-tile's E8M0 scales for 512 K elements are one
+ * contiguous 4 KB block.  For a SWIGLU epilogue an n-tile holds 128 gate
+ * rows and their 128 up rows, in groups of 32 gate then the 32 matching up
+ * rows, so the tiling depends on the epilogue the matrix is used with (FC1:
+ * its SWIGLU layout; FC2: MOE_EPI_NONE).
+ *   w_packed, w_scales  device canonical [E][N][K/2], [E][N][K/32] (input)
+ *   t_packed, t_scales  device out, moe_tiled_weight_bytes(E, N, K, 0 / 1)
+ *                       bytes (the same byte counts as the canonical arrays)
+ * Sizes: E >= 1, K % 512 == 0, N % 256 == 0 (MOE_ERR_SHAPE otherwise);
+ * epilogue a moe_epilogue.  Input and output must not overlap.  Enqueued on
+ * `stream`; nothing else is written.
+ * moe_mxfp4_untile_weights is the exact inverse (tiled -> canonical), with
+ * the same arguments in the other direction.
+ * moe_tiled_weight_bytes returns 0 for sizes the tiling does not take.
+ */
+size_t     moe_tiled_weight_bytes(int32_t E, int32_t N, int32_t K, int32_t which);
+moe_status moe_mxfp4_tile_weights(const uint8_t* w_packed, const uint8_t* w_scales, int32_t E, int32_t N,
+                                  int32_t K, int32_t epilogue, uint8_t* t_packed, uint8_t* t_scales,
+                                  void* stream);
+moe_status moe_mxfp4_untile_weights(const uint8_t* t_packed, const uint8_t* t_scales, int32_t E, int32_t N,
+                                    int32_t K, int32_t epilogue, uint8_t* w_packed, uint8_t* w_scales,
+                                    void* stream);
 
 /* ------------------------------------------------------------ combine -- */
 
@@ -225,6 +266,8 @@ typedef struct moe_layer_args {
   uint16_t*      x_next;         /* device bf16 [T][H] or NULL (see moe_combine) */
   void*          workspace;      /* device, >= moe_layer_workspace_size() */
   size_t         workspace_bytes;
+  int32_t        w_format;       /* moe_weight_format of both weight matrices (tiled: W1
+                                    with `layout`, W2 with MOE_EPI_NONE) */
 } moe_layer_args;
 
 /* Bytes of workspace for a layer of these sizes (routing arrays, the
@@ -297,6 +340,7 @@ typedef struct moe_streamed_args {
                                     end (compute stream) of every layer */
   void*          workspace;      /* device, >= moe_streamed_workspace_size() */
   size_t         workspace_bytes;
+  int32_t        w_format;       /* moe_weight_format of the blobs' W1/S1 and W2/S2 sections */
 } moe_streamed_args;
 
 /* Bytes of one layer's weight blob, and the byte offset of its sections:

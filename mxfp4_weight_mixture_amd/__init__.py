@@ -17,7 +17,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
-ABI_VERSION = 1
+ABI_VERSION = 2
 
 # mirrors of include/mxmoe.h; checked against the library at import
 STATUS = {"MOE_OK": 0, "MOE_ERR_INVALID_ARG": 1, "MOE_ERR_SHAPE": 2, "MOE_ERR_UNSUPPORTED_DEVICE": 3,
@@ -26,7 +26,9 @@ ACT = {"MOE_ACT_BF16": 0, "MOE_ACT_MXFP8_E4M3": 1}
 OUT = {"MOE_OUT_FP32": 0, "MOE_OUT_BF16": 1, "MOE_OUT_MXFP8_E4M3": 2}
 EPI = {"MOE_EPI_NONE": 0, "MOE_EPI_SWIGLU_SPLIT": 1, "MOE_EPI_SWIGLU_INTERLEAVED": 2}
 CHAIN = {"MOE_CHAIN_RMS": 0, "MOE_CHAIN_INDEPENDENT": 1}
-ENUM_KINDS = {0: STATUS, 1: ACT, 2: OUT, 3: EPI, 4: CHAIN}
+WFORMAT = {"MOE_W_CANONICAL": 0, "MOE_W_TILED": 1}
+ENUM_KINDS = {0: STATUS, 1: ACT, 2: OUT, 3: EPI, 4: CHAIN, 5: WFORMAT}
+W_FORMAT = {"canonical": WFORMAT["MOE_W_CANONICAL"], "tiled": WFORMAT["MOE_W_TILED"]}
 
 LAYOUT = {"split": EPI["MOE_EPI_SWIGLU_SPLIT"], "interleaved": EPI["MOE_EPI_SWIGLU_INTERLEAVED"]}
 
@@ -44,14 +46,14 @@ class GemmArgs(ctypes.Structure):
     _fields_ = [("a", _vp), ("a_scales", _vp), ("a_gather", _vp), ("w_packed", _vp), ("w_scales", _vp),
                 ("expert_offsets", _vp), ("c", _vp), ("c_scales", _vp), ("a_dtype", _i32),
                 ("a_gather_div", _i32), ("a_rows", _i32), ("rows", _i32), ("E", _i32), ("N", _i32),
-                ("K", _i32), ("epilogue", _i32), ("c_dtype", _i32)]
+                ("K", _i32), ("epilogue", _i32), ("c_dtype", _i32), ("w_format", _i32)]
 
 
 class LayerArgs(ctypes.Structure):
     _fields_ = [("T", _i32), ("H", _i32), ("I", _i32), ("E", _i32), ("k", _i32), ("layout", _i32),
                 ("act_dtype", _i32), ("inter_dtype", _i32), ("logits", _vp), ("x", _vp), ("x_scales", _vp),
                 ("w1_packed", _vp), ("w1_scales", _vp), ("w2_packed", _vp), ("w2_scales", _vp),
-                ("out", _vp), ("x_next", _vp), ("workspace", _vp), ("workspace_bytes", _sz)]
+                ("out", _vp), ("x_next", _vp), ("workspace", _vp), ("workspace_bytes", _sz), ("w_format", _i32)]
 
 
 class StreamedArgs(ctypes.Structure):
@@ -59,7 +61,7 @@ class StreamedArgs(ctypes.Structure):
                 ("layout", _i32), ("chain", _i32), ("depth", _i32), ("num_blobs", _i32),
                 ("host_blobs", ctypes.POINTER(_vp)), ("blob_bytes", _sz), ("device_slot", _vp * 2),
                 ("logits", _vp), ("x", _vp), ("out", _vp), ("layer_inputs", _vp), ("events", _vp),
-                ("workspace", _vp), ("workspace_bytes", _sz)]
+                ("workspace", _vp), ("workspace_bytes", _sz), ("w_format", _i32)]
 
 
 def _load():
@@ -85,6 +87,9 @@ def _load():
         "moe_blob_section_offset": (_sz, [_i32, _i32, _i32, _i32]),
         "moe_streamed_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32]),
         "moe_layer_prefill_streamed": (ctypes.c_int, [ctypes.POINTER(StreamedArgs), _vp, _vp]),
+        "moe_tiled_weight_bytes": (_sz, [_i32, _i32, _i32, _i32]),
+        "moe_mxfp4_tile_weights": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
+        "moe_mxfp4_untile_weights": (ctypes.c_int, [_vp, _vp, _i32, _i32, _i32, _i32, _vp, _vp, _vp]),
         "moe_layer_graph_create": (ctypes.c_int, [ctypes.POINTER(LayerArgs), _vp, ctypes.POINTER(_vp)]),
         "moe_layer_graph_launch": (ctypes.c_int, [_vp, _vp]),
         "moe_layer_graph_destroy": (ctypes.c_int, [_vp]),
@@ -158,7 +163,8 @@ def permute(topk_ids: torch.Tensor, E: int, stream=None):
 def grouped_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor,
                  expert_offsets: torch.Tensor, *, a_scales: Optional[torch.Tensor] = None,
                  a_gather: Optional[torch.Tensor] = None, a_gather_div: int = 1, rows: Optional[int] = None,
-                 epilogue: str = "none", out_dtype: str = "bf16", stream=None) -> torch.Tensor:
+                 epilogue: str = "none", out_dtype: str = "bf16", w_format: str = "canonical",
+                 stream=None) -> torch.Tensor:
     """moe_mxfp4_grouped_gemm.  a: bf16 [a_rows][K] or uint8 E4M3 codes (with a_scales).
 
     w_packed [E][N][K/2], w_scales [E][N][K/32].  Returns C [rows][N or N/2]
@@ -184,11 +190,35 @@ def grouped_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor
                     expert_offsets=expert_offsets.data_ptr(), c=c.data_ptr(),
                     c_scales=c_scales.data_ptr() if c_scales is not None else None,
                     a_dtype=1 if a_scales is not None else 0, a_gather_div=a_gather_div,
-                    a_rows=a.shape[0], rows=rows, E=E, N=N, K=K, epilogue=epi, c_dtype=c_dt)
+                    a_rows=a.shape[0], rows=rows, E=E, N=N, K=K, epilogue=epi, c_dtype=c_dt,
+                    w_format=W_FORMAT[w_format])
     n = lib.moe_grouped_gemm_workspace_size(ctypes.byref(args))
     ws = _u8(n, a.device)
     _check(lib.moe_mxfp4_grouped_gemm(ctypes.byref(args), _ptr(ws), n, _stream(stream)))
     return (c, c_scales) if c_dt == 2 else c
+
+
+def tile_weights(w_packed: torch.Tensor, w_scales: torch.Tensor, epilogue: str = "none", stream=None):
+    """moe_mxfp4_tile_weights: canonical [E][N][K/2] + [E][N][K/32] -> the tiled order.
+
+    Returns uint8 tensors of the same shapes (the bytes are reordered; the
+    shapes only carry E, N, K).  epilogue: the one the matrix is used with."""
+    E, N, K2 = w_packed.shape
+    tp, ts = torch.empty_like(w_packed), torch.empty_like(w_scales)
+    _check(lib.moe_mxfp4_tile_weights(_ptr(w_packed), _ptr(w_scales), E, N, 2 * K2,
+                                      {"none": 0, "split": 1, "interleaved": 2}[epilogue], _ptr(tp), _ptr(ts),
+                                      _stream(stream)))
+    return tp, ts
+
+
+def untile_weights(t_packed: torch.Tensor, t_scales: torch.Tensor, epilogue: str = "none", stream=None):
+    """moe_mxfp4_untile_weights: the inverse of tile_weights."""
+    E, N, K2 = t_packed.shape
+    wp, ws = torch.empty_like(t_packed), torch.empty_like(t_scales)
+    _check(lib.moe_mxfp4_untile_weights(_ptr(t_packed), _ptr(t_scales), E, N, 2 * K2,
+                                        {"none": 0, "split": 1, "interleaved": 2}[epilogue], _ptr(wp), _ptr(ws),
+                                        _stream(stream)))
+    return wp, ws
 
 
 def combine(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor, *, rms_next: bool = False,
@@ -208,8 +238,18 @@ class Layer:
     """A resident layer: weights stay on the device; forward() runs the five steps on one stream."""
 
     def __init__(self, w1_packed, w1_scales, w2_packed, w2_scales, k: int, layout: str = "split",
-                 inter: str = "bf16"):
-        """inter: precision of the SwiGLU output fed to FC2, "bf16" or "mxfp8"."""
+                 inter: str = "bf16", w_format: str = "canonical", tile: bool = False):
+        """inter: precision of the SwiGLU output fed to FC2, "bf16" or "mxfp8".
+        w_format: the order of the given weights, "canonical" or "tiled" (W1 tiled
+        with `layout`, W2 with "none").  tile=True: canonical weights are tiled
+        here once and the layer keeps only the tiled copy."""
+        if tile:
+            if w_format != "canonical":
+                raise ValueError("tile=True takes canonical weights")
+            w1_packed, w1_scales = tile_weights(w1_packed, w1_scales, layout)
+            w2_packed, w2_scales = tile_weights(w2_packed, w2_scales, "none")
+            w_format = "tiled"
+        self.w_format = W_FORMAT[w_format]
         self.w1p, self.w1s, self.w2p, self.w2s = w1_packed, w1_scales, w2_packed, w2_scales
         self.E, two_i, h2 = w1_packed.shape
         self.I, self.H = two_i // 2, 2 * h2
@@ -229,7 +269,7 @@ class Layer:
                          w1_packed=self.w1p.data_ptr(), w1_scales=self.w1s.data_ptr(),
                          w2_packed=self.w2p.data_ptr(), w2_scales=self.w2s.data_ptr(), out=out.data_ptr(),
                          x_next=x_next.data_ptr() if x_next is not None else None,
-                         workspace=ws.data_ptr(), workspace_bytes=ws.numel())
+                         workspace=ws.data_ptr(), workspace_bytes=ws.numel(), w_format=self.w_format)
 
     def forward(self, logits: torch.Tensor, x: torch.Tensor, x_scales: Optional[torch.Tensor] = None,
                 out: Optional[torch.Tensor] = None, x_next: Optional[torch.Tensor] = None, stream=None):
@@ -325,7 +365,7 @@ def prefill_streamed(host_blobs: Sequence[torch.Tensor], slots: Sequence[torch.T
                      x: torch.Tensor, out: torch.Tensor, *, T: int, H: int, I: int, E: int, k: int,
                      num_layers: int, layout: str = "split", chain: str = "rms", depth: int = 2,
                      layer_inputs: Optional[torch.Tensor] = None, events=None, workspace=None,
-                     compute_stream=None, copy_stream=None):
+                     compute_stream=None, copy_stream=None, w_format: str = "canonical"):
     """moe_layer_prefill_streamed.  host_blobs: pinned uint8 CPU tensors (layer L uses blob L % n)."""
     nb = len(host_blobs)
     arr = (_vp * nb)(*[b.data_ptr() for b in host_blobs])
@@ -343,7 +383,8 @@ def prefill_streamed(host_blobs: Sequence[torch.Tensor], slots: Sequence[torch.T
                         logits=logits.data_ptr(), x=x.data_ptr(), out=out.data_ptr(),
                         layer_inputs=layer_inputs.data_ptr() if layer_inputs is not None else None,
                         events=ctypes.cast(ev_arr, _vp) if ev_arr is not None else None,
-                        workspace=workspace.data_ptr(), workspace_bytes=workspace.numel())
+                        workspace=workspace.data_ptr(), workspace_bytes=workspace.numel(),
+                        w_format=W_FORMAT[w_format])
     cs = _stream(compute_stream)
     xs = _stream(copy_stream) if copy_stream is not None else cs
     _check(lib.moe_layer_prefill_streamed(ctypes.byref(args), cs, xs))

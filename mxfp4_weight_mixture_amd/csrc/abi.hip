@@ -104,6 +104,8 @@ const char* moe_enum_name(int kind, int v) {
              : v == MOE_EPI_SWIGLU_INTERLEAVED ? "MOE_EPI_SWIGLU_INTERLEAVED" : nullptr;
     case MOE_ENUM_CHAIN:
       return v == MOE_CHAIN_RMS ? "MOE_CHAIN_RMS" : v == MOE_CHAIN_INDEPENDENT ? "MOE_CHAIN_INDEPENDENT" : nullptr;
+    case MOE_ENUM_WFORMAT:
+      return v == MOE_W_CANONICAL ? "MOE_W_CANONICAL" : v == MOE_W_TILED ? "MOE_W_TILED" : nullptr;
     default: return nullptr;
   }
 }
@@ -163,6 +165,36 @@ moe_status moe_mxfp4_grouped_gemm(const moe_gemm_args* a, void* workspace, size_
     return fail(MOE_ERR_WORKSPACE, "grouped GEMM: workspace %zu bytes, need %zu", workspace_bytes, need);
   MXMOE_TRY(check_device());
   return launch_gemm(*a, workspace, (hipStream_t)stream);
+}
+
+size_t moe_tiled_weight_bytes(int32_t E, int32_t N, int32_t K, int32_t which) { return tiled_bytes(E, N, K, which); }
+
+static moe_status tile_common(const uint8_t* sp, const uint8_t* ss, int32_t E, int32_t N, int32_t K, int32_t epi,
+                              uint8_t* dp, uint8_t* ds, bool to_tiled, void* stream) {
+  const char* what = to_tiled ? "tile weights" : "untile weights";
+  if (!tile_shape_ok(E, N, K))
+    return fail(MOE_ERR_SHAPE, "%s: needs E >= 1, K %% 512 == 0 and N %% 256 == 0 (E %d, N %d, K %d)", what, E, N, K);
+  if (epi < MOE_EPI_NONE || epi > MOE_EPI_SWIGLU_INTERLEAVED)
+    return fail(MOE_ERR_INVALID_ARG, "%s: bad epilogue %d", what, epi);
+  if (!sp || !ss || !dp || !ds) return fail(MOE_ERR_INVALID_ARG, "%s: null pointer", what);
+  const size_t bp = tiled_bytes(E, N, K, 0), bs = tiled_bytes(E, N, K, 1);
+  auto overlap = [](const uint8_t* a, size_t na, const uint8_t* b, size_t nb) { return a < b + nb && b < a + na; };
+  if (overlap(sp, bp, dp, bp) || overlap(sp, bp, ds, bs) || overlap(ss, bs, dp, bp) || overlap(ss, bs, ds, bs))
+    return fail(MOE_ERR_INVALID_ARG, "%s: input and output overlap", what);
+  MXMOE_TRY(check_device());
+  return launch_tile(sp, ss, E, N, K, epi, dp, ds, to_tiled, (hipStream_t)stream);
+}
+
+moe_status moe_mxfp4_tile_weights(const uint8_t* w_packed, const uint8_t* w_scales, int32_t E, int32_t N, int32_t K,
+                                  int32_t epilogue, uint8_t* t_packed, uint8_t* t_scales, void* stream) {
+  clear_error();
+  return tile_common(w_packed, w_scales, E, N, K, epilogue, t_packed, t_scales, true, stream);
+}
+
+moe_status moe_mxfp4_untile_weights(const uint8_t* t_packed, const uint8_t* t_scales, int32_t E, int32_t N,
+                                    int32_t K, int32_t epilogue, uint8_t* w_packed, uint8_t* w_scales, void* stream) {
+  clear_error();
+  return tile_common(t_packed, t_scales, E, N, K, epilogue, w_packed, w_scales, false, stream);
 }
 
 moe_status moe_combine(const void* y, int32_t y_dtype, const int32_t* dest_row, const float* topk_w,

@@ -78,6 +78,7 @@ struct Params {
   int a_gather_div;
   int N, K, n_out, n_tiles;
   int layout;  // 0 none, 1 split, 2 interleaved
+  int w_tiled; // weights in the load-time tiled order (DMA kernels only)
 };
 
 __device__ inline uint32_t bf16_rne(float f) {
@@ -113,7 +114,11 @@ struct Cfg {
   static constexpr int LDS_BUF = LDS_A + LDS_B + LDS_AS + LDS_BS;
 };
 
-// Row of W (within one expert) that feeds tile column j of n-tile nt.
+// Row of W (within one expert) that feeds tile column j of n-tile nt.  The
+// DMA kernels (and the tiled weight order) use groups of kSwiGroup = 64
+// columns for every tile class; the register-staged kernels use their
+// wave width.
+constexpr int kSwiGroup = 64;
 template <int WN>
 __device__ inline int w_row_of(int layout, int nt, int j, int N, int n_out) {
   if (layout == 0) return min(nt * kBN + j, N - 1);
@@ -584,15 +589,23 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
         a_off[i] = (uint32_t)arow[i] * (uint32_t)a_row_bytes + chunk * 16;
       }
     }
-    const uint8_t* const b_base = p.w + w_expert * (size_t)(K / 2);
+    // B: canonical weights are addressed row by row (tile column j of the
+    // stage's LDS layout <- its weight row); tiled weights already hold the
+    // stage's 16 KB in LDS order, so each instruction copies 1 KB of
+    // consecutive bytes.  b_step / bs_step: bytes from one stage (one scale
+    // group) to the next.
+    const size_t tile_id = (size_t)e * p.n_tiles + nt;
+    const uint8_t* const b_base = p.w_tiled ? p.w + tile_id * (size_t)nst * C::LDS_B : p.w + w_expert * (size_t)(K / 2);
+    const int b_step = p.w_tiled ? C::LDS_B : C::RB;
     uint32_t b_off[C::B_I];
 #pragma unroll
     for (int i = 0; i < C::B_I; ++i) {
       const int line = (wave * C::B_I + i) * 8 + lane / 8;
       const int uu = (lane & 7) ^ b_swz(line);
       const int j = line * 2 + (uu >> 2);
-      const int wr = w_row_of<C::WN>(p.layout, nt, j, p.N, p.n_out);
-      b_off[i] = (uint32_t)wr * (uint32_t)(K / 2) + (uu & 3) * 16;
+      const int wr = w_row_of<kSwiGroup>(p.layout, nt, j, p.N, p.n_out);
+      b_off[i] = p.w_tiled ? (uint32_t)((wave * C::B_I + i) * 1024 + lane * 16)
+                           : (uint32_t)wr * (uint32_t)(K / 2) + (uu & 3) * 16;
     }
     // scale loads: with four waves every wave loads 64 rows of A scales (if
     // below BM) and 64 of B scales; with eight, waves 0-3 load A, 4-7 load B
@@ -606,8 +619,11 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
       const int r = min(srow, mrows - 1);
       as_off = (uint32_t)(gather ? p.a_gather[row0 + r] / p.a_gather_div : r) * (uint32_t)kb;
     }
-    const uint8_t* const bs_base = p.w_scales + w_expert * (size_t)kb;
-    const uint32_t bs_off = (uint32_t)w_row_of<C::WN>(p.layout, nt, srow, p.N, p.n_out) * (uint32_t)kb;
+    const uint8_t* const bs_base =
+        p.w_tiled ? p.w_scales + tile_id * (size_t)(K / 512) * 4096 : p.w_scales + w_expert * (size_t)kb;
+    const int bs_step = p.w_tiled ? 4096 : 16;
+    const uint32_t bs_off = p.w_tiled ? (uint32_t)(sw * 1024 + lane * 16)
+                                      : (uint32_t)w_row_of<kSwiGroup>(p.layout, nt, srow, p.N, p.n_out) * (uint32_t)kb;
     uint8_t* const sg = lds + C::NST * C::LDS_STAGE;   // two scale groups
 
     const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
@@ -620,20 +636,20 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
       for (int i = 0; i < C::A_I; ++i) dma16(ra, a_off[i], s * C::RA, base + (wave * C::A_I + i) * 1024);
 #pragma unroll
       for (int i = 0; i < C::B_I; ++i)
-        dma16(rb, b_off[i], s * C::RB, base + C::LDS_A + (wave * C::B_I + i) * 1024);
+        dma16(rb, b_off[i], s * b_step, base + C::LDS_A + (wave * C::B_I + i) * 1024);
     };
     // DMA instruction j of stage s (j < A_I: A, then B), for interleaving with products
     auto issue_one = [&](int s, int j) {
       uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
       if (j < C::A_I) dma16(ra, a_off[j], s * C::RA, base + (wave * C::A_I + j) * 1024);
-      else dma16(rb, b_off[j - C::A_I], s * C::RB, base + C::LDS_A + (wave * C::B_I + j - C::A_I) * 1024);
+      else dma16(rb, b_off[j - C::A_I], s * b_step, base + C::LDS_A + (wave * C::B_I + j - C::A_I) * 1024);
     };
     // scale group j (stages 4j..4j+3): 16 bytes of every A and B row
     auto issue_scales = [&](int j) {
       uint8_t* base = sg + (j & 1) * C::LDS_SG;
       // (a 32-row tile has 512 bytes of A scales per group: lanes 32-63 stay idle)
       if (FP8 && a_sw && sw * 64 < BM && (BM >= 64 || lane < BM)) dma16(ras, as_off, 16 * j, base + sw * 1024);
-      if (b_sw) dma16(rbs, bs_off, 16 * j, base + C::SG_A + sw * 1024);
+      if (b_sw) dma16(rbs, bs_off, bs_step * j, base + C::SG_A + sw * 1024);
     };
 
     v16f acc[C::FM][C::FN];
@@ -914,8 +930,9 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
     }
 
     // ---- epilogue: registers -> C in permuted row order ----
-    // gate/up pairing of the SwiGLU layouts: this wave's fragment fh holds gate
-    // columns, fragment fh + FN/2 the matching up columns
+    // gate/up pairing of the SwiGLU layouts: columns come in groups of 64, 32
+    // gate rows then their 32 up rows, so fragment 2fh holds gate columns and
+    // fragment 2fh + 1 the matching up columns
     constexpr int HF = C::FN / 2;
     if constexpr (OUT == MOE_OUT_FP32) {
       // fp32: straight from the accumulators, one fragment at a time
@@ -942,7 +959,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
               const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
+              const float a = silu_mul(acc[fm][2 * fh][q], acc[fm][2 * fh + 1][q]);
               if (r < mrows && i < p.n_out) static_cast<float*>(p.c)[(size_t)(row0 + r) * p.n_out + i] = a;
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -980,7 +997,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
               const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
+              const float a = silu_mul(acc[fm][2 * fh][q], acc[fm][2 * fh + 1][q]);
               if constexpr (MX) *reinterpret_cast<float*>(col + r * PITCH) = a;
               else *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)a;
             }
@@ -1052,6 +1069,79 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
     if (threadIdx.x == 0) *unit_slot = u_next;
     stage_barrier();
     u = u_first + *unit_slot;
+  }
+}
+
+// ---- load-time weight tiling ------------------------------------------
+//
+// Tiled order of one weight matrix (kept instead of the canonical one): for
+// expert e, n-tile nt and 128-element stage s, the 16 KB block at
+// ((e * n_tiles + nt) * nst + s) * 16384 holds at byte q exactly what the DMA
+// kernels' B load puts at byte q of the stage's LDS B area (line q / 128 =
+// tile columns 2*line, 2*line + 1; slot (q % 128) / 16 XOR the line swizzle
+// -> column 2*line + slot' / 4, 16-byte chunk slot' % 4 of its 64 stage
+// bytes).  Scales: for scale group g (512 K elements) the 4 KB block at
+// ((e * n_tiles + nt) * (K / 512) + g) * 4096 holds at byte 16c + b scale
+// byte 16g + b of tile column c's row.  Needs K % 512 == 0 and N % 256 == 0,
+// so every tile column is one distinct weight row and the map is a bijection.
+
+// canonical row r -> (n-tile, tile column): the inverse of w_row_of<kSwiGroup>
+__device__ inline void tile_col_of(int layout, int r, int n_out, int& nt, int& j) {
+  if (layout == 0) {
+    nt = r / kBN;
+    j = r % kBN;
+    return;
+  }
+  const int up = layout == 1 ? (r >= n_out ? 1 : 0) : (r & 1);
+  const int i = layout == 1 ? r - up * n_out : r >> 1;
+  nt = i / (kBN / 2);
+  const int ii = i % (kBN / 2);
+  j = (ii / 32) * kSwiGroup + up * 32 + ii % 32;
+}
+
+// one thread per 16-byte chunk of the canonical packed matrix
+template <bool TO_TILED>
+__global__ __launch_bounds__(256) void tile_packed_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                          int E, int N, int K, int layout) {
+  const int cpr = K / 32;   // 16-byte chunks per row (K/2 bytes)
+  const int64_t total = (int64_t)E * N * cpr;
+  const int n_tiles = N / kBN, nst = K / 128;
+  const int n_out = layout == 0 ? N : N / 2;
+  for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total; id += (int64_t)gridDim.x * 256) {
+    const int c = (int)(id % cpr);
+    const int64_t er = id / cpr;
+    const int r = (int)(er % N);
+    const int e = (int)(er / N);
+    int nt, j;
+    tile_col_of(layout, r, n_out, nt, j);
+    const int line = j >> 1;
+    const int slot = ((j & 1) * 4 + (c & 3)) ^ b_swz(line);
+    const int64_t t = (((int64_t)e * n_tiles + nt) * nst + (c >> 2)) * 16384 + line * 128 + slot * 16;
+    const int64_t cp = er * (K / 2) + (int64_t)c * 16;
+    if (TO_TILED) *reinterpret_cast<uint4*>(dst + t) = *reinterpret_cast<const uint4*>(src + cp);
+    else *reinterpret_cast<uint4*>(dst + cp) = *reinterpret_cast<const uint4*>(src + t);
+  }
+}
+
+// one thread per 16-byte scale group of a canonical row
+template <bool TO_TILED>
+__global__ __launch_bounds__(256) void tile_scales_kernel(const uint8_t* __restrict__ src, uint8_t* __restrict__ dst,
+                                                          int E, int N, int K, int layout) {
+  const int gpr = K / 512;
+  const int64_t total = (int64_t)E * N * gpr;
+  const int n_tiles = N / kBN;
+  const int n_out = layout == 0 ? N : N / 2;
+  for (int64_t id = (int64_t)blockIdx.x * 256 + threadIdx.x; id < total; id += (int64_t)gridDim.x * 256) {
+    const int g = (int)(id % gpr);
+    const int64_t er = id / gpr;
+    const int r = (int)(er % N);
+    const int e = (int)(er / N);
+    int nt, j;
+    tile_col_of(layout, r, n_out, nt, j);
+    const int64_t t = (((int64_t)e * n_tiles + nt) * gpr + g) * 4096 + j * 16;
+    const int64_t cp = er * (K / 32) + (int64_t)g * 16;
+    if (TO_TILED) *reinterpret_cast<uint4*>(dst + t) = *reinterpret_cast<const uint4*>(src + cp);
+    else *reinterpret_cast<uint4*>(dst + cp) = *reinterpret_cast<const uint4*>(src + t);
   }
 }
 
@@ -1249,6 +1339,32 @@ moe_status validate_gemm(const moe_gemm_args& a) {
   }
   if (!a.a_gather && a.a_rows < a.rows)
     return fail(MOE_ERR_SHAPE, "grouped GEMM: A has %d rows, fewer than rows %d", a.a_rows, a.rows);
+  if (a.w_format != MOE_W_CANONICAL && a.w_format != MOE_W_TILED)
+    return fail(MOE_ERR_INVALID_ARG, "grouped GEMM: bad w_format %d", a.w_format);
+  if (a.w_format == MOE_W_TILED && (a.K % 512 || a.N % 256))
+    return fail(MOE_ERR_SHAPE, "grouped GEMM: tiled weights need K %% 512 == 0 and N %% 256 == 0 (K %d, N %d)",
+                a.K, a.N);
+  return MOE_OK;
+}
+
+bool tile_shape_ok(int E, int N, int K) { return E >= 1 && N >= 256 && K >= 512 && N % 256 == 0 && K % 512 == 0; }
+
+size_t tiled_bytes(int E, int N, int K, int which) {
+  if (!tile_shape_ok(E, N, K) || (which != 0 && which != 1)) return 0;
+  return (size_t)E * N * (which == 0 ? K / 2 : K / 32);
+}
+
+moe_status launch_tile(const uint8_t* src_p, const uint8_t* src_s, int E, int N, int K, int layout,
+                       uint8_t* dst_p, uint8_t* dst_s, bool to_tiled, hipStream_t s) {
+  const int grid = num_cus() * 8;
+  if (to_tiled) {
+    hipLaunchKernelGGL(tile_packed_kernel<true>, dim3(grid), dim3(256), 0, s, src_p, dst_p, E, N, K, layout);
+    hipLaunchKernelGGL(tile_scales_kernel<true>, dim3(grid), dim3(256), 0, s, src_s, dst_s, E, N, K, layout);
+  } else {
+    hipLaunchKernelGGL(tile_packed_kernel<false>, dim3(grid), dim3(256), 0, s, src_p, dst_p, E, N, K, layout);
+    hipLaunchKernelGGL(tile_scales_kernel<false>, dim3(grid), dim3(256), 0, s, src_s, dst_s, E, N, K, layout);
+  }
+  MXMOE_HIP(hipGetLastError());
   return MOE_OK;
 }
 
@@ -1282,6 +1398,7 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
   p.N = a.N;
   p.K = a.K;
   p.layout = a.epilogue;
+  p.w_tiled = a.w_format == MOE_W_TILED ? 1 : 0;
   if (a.epilogue == MOE_EPI_NONE) {
     p.n_out = a.N;
     p.n_tiles = (a.N + kBN - 1) / kBN;

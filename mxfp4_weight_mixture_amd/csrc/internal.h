@@ -45,6 +45,11 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s);
 moe_status launch_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* w,
                           int T, int k, int H, float* out, uint16_t* x_next, hipStream_t s);
 moe_status validate_gemm(const moe_gemm_args& a);
+// load-time weight tiling (gemm.hip)
+bool tile_shape_ok(int E, int N, int K);
+size_t tiled_bytes(int E, int N, int K, int which);
+moe_status launch_tile(const uint8_t* src_p, const uint8_t* src_s, int E, int N, int K, int layout,
+                       uint8_t* dst_p, uint8_t* dst_s, bool to_tiled, hipStream_t s);
 
 // ---- layer workspace layout -------------------------------------------
 struct LayerWs {

@@ -57,6 +57,15 @@ moe_status validate_layer_sizes(int T, int H, int I, int E, int k, int layout, i
   return MOE_OK;
 }
 
+// tiled weights: FC1 (K = H, N = 2I) and FC2 (K = I, N = H) must both be tileable
+moe_status validate_w_format(int w_format, int H, int I) {
+  if (w_format != MOE_W_CANONICAL && w_format != MOE_W_TILED)
+    return fail(MOE_ERR_INVALID_ARG, "layer: bad w_format %d", w_format);
+  if (w_format == MOE_W_TILED && (H % 512 || I % 512))
+    return fail(MOE_ERR_SHAPE, "layer: tiled weights need H %% 512 == 0 and I %% 512 == 0 (H %d, I %d)", H, I);
+  return MOE_OK;
+}
+
 // The body of a layer, all arguments valid; pointers into `ws`.
 moe_status run_layer(const moe_layer_args& a, hipStream_t s) {
   if (a.T == 0) return MOE_OK;
@@ -90,6 +99,7 @@ moe_status run_layer(const moe_layer_args& a, hipStream_t s) {
   g1.c = ws + L.inter;
   g1.c_scales = a.inter_dtype == MOE_OUT_MXFP8_E4M3 ? ws + L.inter_scales : nullptr;
   g1.c_dtype = a.inter_dtype;
+  g1.w_format = a.w_format;
   MXMOE_TRY(launch_gemm(g1, ws + L.gemm_ws, s));
 
   moe_gemm_args g2{};
@@ -109,6 +119,7 @@ moe_status run_layer(const moe_layer_args& a, hipStream_t s) {
   g2.epilogue = MOE_EPI_NONE;
   g2.c = ws + L.y;
   g2.c_dtype = MOE_OUT_BF16;
+  g2.w_format = a.w_format;
   MXMOE_TRY(launch_gemm(g2, ws + L.gemm_ws, s));
 
   return launch_combine(ws + L.y, MOE_OUT_BF16, dest_row, w, a.T, a.k, a.H, a.out, a.x_next, s);
@@ -199,6 +210,7 @@ moe_status moe_layer_forward(const moe_layer_args* a, void* stream) {
   clear_error();
   if (!a) return fail(MOE_ERR_INVALID_ARG, "layer: null args");
   MXMOE_TRY(validate_layer_sizes(a->T, a->H, a->I, a->E, a->k, a->layout, a->act_dtype, a->inter_dtype));
+  MXMOE_TRY(validate_w_format(a->w_format, a->H, a->I));
   if (a->T > 0 && (!a->logits || !a->x || !a->w1_packed || !a->w1_scales || !a->w2_packed ||
                    !a->w2_scales || !a->out))
     return fail(MOE_ERR_INVALID_ARG, "layer: null pointer");
@@ -237,6 +249,7 @@ moe_status moe_layer_prefill_streamed(const moe_streamed_args* a, void* compute_
   clear_error();
   if (!a) return fail(MOE_ERR_INVALID_ARG, "streamed: null args");
   MXMOE_TRY(validate_layer_sizes(a->T, a->H, a->I, a->E, a->k, a->layout, MOE_ACT_BF16, MOE_OUT_BF16));
+  MXMOE_TRY(validate_w_format(a->w_format, a->H, a->I));
   if (a->num_layers < 1) return fail(MOE_ERR_SHAPE, "streamed: num_layers = %d < 1", a->num_layers);
   if (a->depth != 1 && a->depth != 2) return fail(MOE_ERR_INVALID_ARG, "streamed: depth %d must be 1 or 2", a->depth);
   if (a->chain != MOE_CHAIN_RMS && a->chain != MOE_CHAIN_INDEPENDENT)
@@ -316,6 +329,7 @@ moe_status moe_layer_prefill_streamed(const moe_streamed_args* a, void* compute_
     la.x_next = x_next;
     la.workspace = ws + sw.layer;
     la.workspace_bytes = sw.out_tmp - sw.layer;
+    la.w_format = a->w_format;
     MXMOE_TRY(run_layer(la, cs));
     if (user_ev) MXMOE_HIP(hipEventRecord(user_ev[4 * L + 3], cs));
     MXMOE_HIP(hipEventRecord(computed[slot], cs));

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_abi_version_and_enum_names():
-    assert mx.lib.moe_abi_version() == mx.ABI_VERSION == 1
+    assert mx.lib.moe_abi_version() == mx.ABI_VERSION == 2
     # each enum value round-trips through the library's names (the binding checked it at import too)
     for kind, table in mx.ENUM_KINDS.items():
         for name, value in table.items():
@@ -139,3 +139,36 @@ def test_layer_graph_argument_errors():
     assert mx.lib.moe_layer_graph_destroy(None) == 0
     st, msg = _status(mx.lib.moe_layer_graph_launch(None, None))
     assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "handle" in msg
+
+
+def test_weight_tiling_sizes_and_argument_errors():
+    """The tiled order keeps the canonical byte counts; shapes it does not take
+    (K % 512, N % 256) and bad arguments are refused before any device call,
+    and a grouped GEMM or layer that names tiled weights of such a shape too."""
+    E, N, K = 3, 512, 1024
+    assert mx.lib.moe_tiled_weight_bytes(E, N, K, 0) == E * N * K // 2
+    assert mx.lib.moe_tiled_weight_bytes(E, N, K, 1) == E * N * K // 32
+    assert mx.lib.moe_tiled_weight_bytes(E, 384, K, 0) == 0 and mx.lib.moe_tiled_weight_bytes(E, N, 768, 1) == 0
+    assert mx.lib.moe_tiled_weight_bytes(E, N, K, 2) == 0
+    p = ctypes.c_void_p(16)
+    st, msg = _status(mx.lib.moe_mxfp4_tile_weights(p, p, E, 384, K, 0, p, p, None))
+    assert st == mx.STATUS["MOE_ERR_SHAPE"] and "N % 256" in msg
+    st, msg = _status(mx.lib.moe_mxfp4_untile_weights(p, p, E, N, 640, 0, p, p, None))
+    assert st == mx.STATUS["MOE_ERR_SHAPE"] and "K % 512" in msg
+    st, msg = _status(mx.lib.moe_mxfp4_tile_weights(p, p, E, N, K, 3, p, p, None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "epilogue" in msg
+    st, msg = _status(mx.lib.moe_mxfp4_tile_weights(None, p, E, N, K, 0, p, p, None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "null" in msg
+    a, b = ctypes.c_void_p(1 << 20), ctypes.c_void_p((1 << 20) + 4096)
+    st, msg = _status(mx.lib.moe_mxfp4_tile_weights(a, ctypes.c_void_p(1 << 30), E, N, K, 0, b,
+                                                    ctypes.c_void_p(1 << 31), None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "overlap" in msg
+    args = _gemm_args(K=640, w_format=1)
+    st, msg = _status(mx.lib.moe_mxfp4_grouped_gemm(ctypes.byref(args), ctypes.c_void_p(16), 1 << 20, None))
+    assert st == mx.STATUS["MOE_ERR_SHAPE"] and "tiled" in msg
+    args = _gemm_args(w_format=7)
+    st, msg = _status(mx.lib.moe_mxfp4_grouped_gemm(ctypes.byref(args), ctypes.c_void_p(16), 1 << 20, None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "w_format" in msg
+    largs = mx.LayerArgs(T=4, H=512, I=256, E=4, k=2, layout=1, act_dtype=0, inter_dtype=1, w_format=1)
+    st, msg = _status(mx.lib.moe_layer_forward(ctypes.byref(largs), None))
+    assert st == mx.STATUS["MOE_ERR_SHAPE"] and "tiled" in msg

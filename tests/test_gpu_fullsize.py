@@ -93,3 +93,22 @@ def test_prefill896_repeat_runs_bitwise_identical():
     for _ in range(4):
         assert torch.equal(layer.forward(logits, x, xs), first)
     assert torch.isfinite(first).all()
+
+
+@pytest.mark.parametrize("name,over,inter", [("prefill896_mxfp8", {}, "mxfp8"), ("decode", {"T": 32}, "bf16"),
+                                             ("prefill256", {}, "bf16")])
+def test_full_size_tiled_weights_equal_canonical_bitwise(name, over, inter):
+    """The benchmark's configuration runs on load-time tiled weights; at the full
+    sizes its layer output equals the canonical-weight layer's bitwise."""
+    s = gen.preset(name, **over)
+    li = gen.layer_inputs(s)
+    w = device_weights(s)
+    x, xs = device_x(li)
+    logits = torch.from_numpy(li.logits).to(DEV)
+    ref = mx.Layer(*w, k=s.k, layout=s.layout, inter=inter).forward(logits, x, xs).clone()
+    tiled = mx.Layer(*w, k=s.k, layout=s.layout, inter=inter, tile=True)
+    del w
+    got = tiled.forward(logits, x, xs)
+    torch.cuda.synchronize()
+    assert torch.equal(ref, got)
+    print(f"[{name}] tiled == canonical bitwise", flush=True)
