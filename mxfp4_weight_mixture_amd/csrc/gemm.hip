@@ -78,7 +78,6 @@ struct Params {
   int a_gather_div;
   int N, K, n_out, n_tiles;
   int layout;  // 0 none, 1 split, 2 interleaved
-  int w_tiled; // weights in the load-time tiled order (DMA kernels only)
 };
 
 __device__ inline uint32_t bf16_rne(float f) {
@@ -505,7 +504,7 @@ __device__ inline int mxfp8_block_exp(float amax) {
 // one barrier in the middle of each stage that both publishes stage s+1 and
 // frees stage s's buffer for the DMA of stage s+3.  bf16 operands: the
 // stage's reads and products follow one barrier at its start.
-template <int BM, bool FP8, int EPI, int OUT>
+template <int BM, bool FP8, int EPI, int OUT, bool TILED>
 __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_kernel(Params p) {
   using C = Cfg2<BM, FP8, dma_waves<BM, FP8, EPI>()>;
   __shared__ __attribute__((aligned(1024))) uint8_t lds[C::LDS_TOTAL];
@@ -546,6 +545,11 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
     const int wn0 = (wave % C::WAVES_N) * C::WN;
     const int l32 = lane & 31;
     const int g = lane >> 5;
+    // 32-column block of the tile that B fragment j of this wave reads.  Tile
+    // columns come in groups of 64 (32 gate rows, then their 32 up rows) for
+    // every tile class; with a SwiGLU epilogue the wave's fragments are ordered
+    // gate blocks first, so that fragment fh and fh + FN/2 pair up.
+    auto frag_block = [](int j) { return EPI == 0 ? j : (j % (C::FN / 2)) * 2 + j / (C::FN / 2); };
     // fragment rows / lines start at multiples of 16, so the swizzles depend on the lane only
     const int xa = a_swz<FP8>(l32 & 15);
     const int xb = b_swz((l32 >> 1) & 7);
@@ -595,8 +599,8 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
     // consecutive bytes.  b_step / bs_step: bytes from one stage (one scale
     // group) to the next.
     const size_t tile_id = (size_t)e * p.n_tiles + nt;
-    const uint8_t* const b_base = p.w_tiled ? p.w + tile_id * (size_t)nst * C::LDS_B : p.w + w_expert * (size_t)(K / 2);
-    const int b_step = p.w_tiled ? C::LDS_B : C::RB;
+    const uint8_t* const b_base = TILED ? p.w + tile_id * (size_t)nst * C::LDS_B : p.w + w_expert * (size_t)(K / 2);
+    const int b_step = TILED ? C::LDS_B : C::RB;
     uint32_t b_off[C::B_I];
 #pragma unroll
     for (int i = 0; i < C::B_I; ++i) {
@@ -604,7 +608,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
       const int uu = (lane & 7) ^ b_swz(line);
       const int j = line * 2 + (uu >> 2);
       const int wr = w_row_of<kSwiGroup>(p.layout, nt, j, p.N, p.n_out);
-      b_off[i] = p.w_tiled ? (uint32_t)((wave * C::B_I + i) * 1024 + lane * 16)
+      b_off[i] = TILED ? (uint32_t)((wave * C::B_I + i) * 1024 + lane * 16)
                            : (uint32_t)wr * (uint32_t)(K / 2) + (uu & 3) * 16;
     }
     // scale loads: with four waves every wave loads 64 rows of A scales (if
@@ -620,9 +624,9 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
       as_off = (uint32_t)(gather ? p.a_gather[row0 + r] / p.a_gather_div : r) * (uint32_t)kb;
     }
     const uint8_t* const bs_base =
-        p.w_tiled ? p.w_scales + tile_id * (size_t)(K / 512) * 4096 : p.w_scales + w_expert * (size_t)kb;
-    const int bs_step = p.w_tiled ? 4096 : 16;
-    const uint32_t bs_off = p.w_tiled ? (uint32_t)(sw * 1024 + lane * 16)
+        TILED ? p.w_scales + tile_id * (size_t)(K / 512) * 4096 : p.w_scales + w_expert * (size_t)kb;
+    const int bs_step = TILED ? 4096 : 16;
+    const uint32_t bs_off = TILED ? (uint32_t)(sw * 1024 + lane * 16)
                                       : (uint32_t)w_row_of<kSwiGroup>(p.layout, nt, srow, p.N, p.n_out) * (uint32_t)kb;
     uint8_t* const sg = lds + C::NST * C::LDS_STAGE;   // two scale groups
 
@@ -674,7 +678,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
       auto read_frag = [&](int s, int kk, int j, v8i (&af)[C::FM], v4i (&bq)[C::FN]) {
         const uint8_t* la = stage_lds(s);
         if (j < C::FN) {
-          const int n = wn0 + j * 32 + l32;
+          const int n = wn0 + frag_block(j) * 32 + l32;
           const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xb;
           bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
         } else {
@@ -692,7 +696,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
       auto read_scale = [&](int s, int j, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
         const uint8_t* lsg = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4);
         if (j < C::FM) ta[j] = *reinterpret_cast<const uint32_t*>(lsg + (wm0 + j * 32 + l32) * 16);
-        else tb[j - C::FM] = *reinterpret_cast<const uint32_t*>(lsg + C::SG_A + (wn0 + (j - C::FM) * 32 + l32) * 16);
+        else tb[j - C::FM] = *reinterpret_cast<const uint32_t*>(lsg + C::SG_A + (wn0 + frag_block(j - C::FM) * 32 + l32) * 16);
       };
       // product i of one k-half, B-fragment major.  ta/tb hold this lane's scale
       // bytes in the order the op_sel field reads them: byte kk = block 2kk + g.
@@ -820,7 +824,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
       auto read_frag = [&](int s, int h, int j, v4i (&bq)[C::FN], v8bf (&af)[4][C::FM]) {
         const uint8_t* la = stage_lds(s);
         if (j < C::FN) {
-          const int n = wn0 + j * 32 + l32;
+          const int n = wn0 + frag_block(j) * 32 + l32;
           const int uu = ((n & 1) * 4 + 2 * h + g) ^ xb;
           bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
         } else {
@@ -832,7 +836,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
       };
       auto read_scale = [&](int s, int j, uint32_t (&tb)[C::FN]) {
         const uint8_t* lsb = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4) + C::SG_A;
-        tb[j] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + j * 32 + l32) * 16);
+        tb[j] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + frag_block(j) * 32 + l32) * 16);
       };
       // conversion unit (fn, d): the 8 weights of bw[fn][d] (E2M1 x block scale -> bf16, exact)
       auto expand = [&](int h, int fn, int d, const v4i (&bq)[C::FN], const uint32_t (&tb)[C::FN]) {
@@ -930,9 +934,9 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
     }
 
     // ---- epilogue: registers -> C in permuted row order ----
-    // gate/up pairing of the SwiGLU layouts: columns come in groups of 64, 32
-    // gate rows then their 32 up rows, so fragment 2fh holds gate columns and
-    // fragment 2fh + 1 the matching up columns
+    // gate/up pairing of the SwiGLU layouts: fragment fh holds the gate columns
+    // of 32-column block 2fh, fragment fh + FN/2 the matching up columns of
+    // block 2fh + 1 (see frag_block)
     constexpr int HF = C::FN / 2;
     if constexpr (OUT == MOE_OUT_FP32) {
       // fp32: straight from the accumulators, one fragment at a time
@@ -959,7 +963,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
               const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              const float a = silu_mul(acc[fm][2 * fh][q], acc[fm][2 * fh + 1][q]);
+              const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
               if (r < mrows && i < p.n_out) static_cast<float*>(p.c)[(size_t)(row0 + r) * p.n_out + i] = a;
             }
             __builtin_amdgcn_sched_barrier(0);
@@ -997,7 +1001,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
               const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              const float a = silu_mul(acc[fm][2 * fh][q], acc[fm][2 * fh + 1][q]);
+              const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
               if constexpr (MX) *reinterpret_cast<float*>(col + r * PITCH) = a;
               else *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)a;
             }
@@ -1234,22 +1238,25 @@ int persistent_grid(KernelT kernel, int threads = kThreads) {
   return (grid + kXcds - 1) / kXcds * kXcds;
 }
 
-template <int BM, bool FP8, int EPI, int OUT, bool DMA>
+// PATH: 0 register-staged kernels, 1 DMA kernels on canonical weights, 2 DMA
+// kernels on tiled weights
+template <int BM, bool FP8, int EPI, int OUT, int PATH>
 int class_grid() {
   static int grid = 0;  // per instantiation; one device type (gfx950)
   if (grid == 0) {
-    if constexpr (DMA) grid = persistent_grid(gemm_dma_kernel<BM, FP8, EPI, OUT>, 64 * dma_waves<BM, FP8, EPI>());
+    if constexpr (PATH != 0)
+      grid = persistent_grid(gemm_dma_kernel<BM, FP8, EPI, OUT, PATH == 2>, 64 * dma_waves<BM, FP8, EPI>());
     else grid = persistent_grid(gemm_kernel<BM, FP8, EPI, OUT>);
   }
   return grid;
 }
 
-template <int BM, bool FP8, int EPI, int OUT, bool DMA>
+template <int BM, bool FP8, int EPI, int OUT, int PATH>
 moe_status launch_class(const Params& p, hipStream_t s) {
-  const int grid = class_grid<BM, FP8, EPI, OUT, DMA>();
-  if constexpr (DMA)
-    hipLaunchKernelGGL((gemm_dma_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(64 * dma_waves<BM, FP8, EPI>()), 0,
-                       s, p);
+  const int grid = class_grid<BM, FP8, EPI, OUT, PATH>();
+  if constexpr (PATH != 0)
+    hipLaunchKernelGGL((gemm_dma_kernel<BM, FP8, EPI, OUT, PATH == 2>), dim3(grid),
+                       dim3(64 * dma_waves<BM, FP8, EPI>()), 0, s, p);
   else
     hipLaunchKernelGGL((gemm_kernel<BM, FP8, EPI, OUT>), dim3(grid), dim3(kThreads), 0, s, p);
   MXMOE_HIP(hipGetLastError());
@@ -1260,7 +1267,7 @@ moe_status launch_class(const Params& p, hipStream_t s) {
 // the HBM-bound small-tile classes beside the full-tile class on a slice of
 // the CUs was measured slower: a few CUs cannot pull the weight stream at
 // HBM rate, and the full tiles lose those CUs for longer.)
-template <bool FP8, int EPI, int OUT, bool DMA>
+template <bool FP8, int EPI, int OUT, int PATH>
 moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* counts, hipStream_t s) {
   int32_t* const ctr = p.unit_ctr;
   auto at = [&](int c) {
@@ -1268,32 +1275,41 @@ moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* count
     p.tile_count = counts + c;
     p.unit_ctr = ctr + c * kXcds;
   };
-  at(0); MXMOE_TRY((launch_class<32, FP8, EPI, OUT, DMA>(p, s)));
-  at(1); MXMOE_TRY((launch_class<64, FP8, EPI, OUT, DMA>(p, s)));
-  at(2); MXMOE_TRY((launch_class<128, FP8, EPI, OUT, DMA>(p, s)));
+  at(0); MXMOE_TRY((launch_class<32, FP8, EPI, OUT, PATH>(p, s)));
+  at(1); MXMOE_TRY((launch_class<64, FP8, EPI, OUT, PATH>(p, s)));
+  at(2); MXMOE_TRY((launch_class<128, FP8, EPI, OUT, PATH>(p, s)));
   // the bf16 DMA kernel's full tile is 128 rows (its 256-row stages do not fit
   // in LDS), so its class-3 list is empty
-  if constexpr (!(DMA && !FP8)) {
-    at(3); MXMOE_TRY((launch_class<256, FP8, EPI, OUT, DMA>(p, s)));
+  if constexpr (!(PATH != 0 && !FP8)) {
+    at(3); MXMOE_TRY((launch_class<256, FP8, EPI, OUT, PATH>(p, s)));
   }
   return MOE_OK;
 }
 
-template <bool FP8, int EPI, bool DMA>
+template <bool FP8, int EPI, int PATH>
 moe_status dispatch_out(const Params& p, int c_dtype, const Tile* lists, int cap,
                         const int32_t* counts, hipStream_t s) {
-  if (c_dtype == MOE_OUT_FP32) return launch_all<FP8, EPI, MOE_OUT_FP32, DMA>(p, lists, cap, counts, s);
-  if (c_dtype == MOE_OUT_BF16) return launch_all<FP8, EPI, MOE_OUT_BF16, DMA>(p, lists, cap, counts, s);
-  if constexpr (DMA && EPI != 0) return launch_all<FP8, EPI, MOE_OUT_MXFP8_E4M3, DMA>(p, lists, cap, counts, s);
+  if (c_dtype == MOE_OUT_FP32) return launch_all<FP8, EPI, MOE_OUT_FP32, PATH>(p, lists, cap, counts, s);
+  if (c_dtype == MOE_OUT_BF16) return launch_all<FP8, EPI, MOE_OUT_BF16, PATH>(p, lists, cap, counts, s);
+  if constexpr (PATH != 0 && EPI != 0)
+    return launch_all<FP8, EPI, MOE_OUT_MXFP8_E4M3, PATH>(p, lists, cap, counts, s);
   return fail(MOE_ERR_NOT_IMPLEMENTED,
               "grouped GEMM: MXFP8 output needs the SwiGLU epilogue and K %% 512 == 0");
 }
 
-template <bool FP8, bool DMA>
+template <bool FP8, int PATH>
 moe_status dispatch_epi(const Params& p, int epi, int c_dtype, const Tile* lists, int cap,
                         const int32_t* counts, hipStream_t s) {
-  if (epi == MOE_EPI_NONE) return dispatch_out<FP8, 0, DMA>(p, c_dtype, lists, cap, counts, s);
-  return dispatch_out<FP8, 1, DMA>(p, c_dtype, lists, cap, counts, s);
+  if (epi == MOE_EPI_NONE) return dispatch_out<FP8, 0, PATH>(p, c_dtype, lists, cap, counts, s);
+  return dispatch_out<FP8, 1, PATH>(p, c_dtype, lists, cap, counts, s);
+}
+
+template <bool FP8>
+moe_status dispatch_path(int path, const Params& p, int epi, int c_dtype, const Tile* lists, int cap,
+                         const int32_t* counts, hipStream_t s) {
+  if (path == 2) return dispatch_epi<FP8, 2>(p, epi, c_dtype, lists, cap, counts, s);
+  if (path == 1) return dispatch_epi<FP8, 1>(p, epi, c_dtype, lists, cap, counts, s);
+  return dispatch_epi<FP8, 0>(p, epi, c_dtype, lists, cap, counts, s);
 }
 
 }  // namespace
@@ -1398,7 +1414,6 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
   p.N = a.N;
   p.K = a.K;
   p.layout = a.epilogue;
-  p.w_tiled = a.w_format == MOE_W_TILED ? 1 : 0;
   if (a.epilogue == MOE_EPI_NONE) {
     p.n_out = a.N;
     p.n_tiles = (a.N + kBN - 1) / kBN;
@@ -1406,11 +1421,9 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
     p.n_out = a.N / 2;
     p.n_tiles = (p.n_out + kBN / 2 - 1) / (kBN / 2);
   }
-  if (fp8)
-    return dma ? dispatch_epi<true, true>(p, a.epilogue, a.c_dtype, lists, cap, counts, s)
-               : dispatch_epi<true, false>(p, a.epilogue, a.c_dtype, lists, cap, counts, s);
-  return dma ? dispatch_epi<false, true>(p, a.epilogue, a.c_dtype, lists, cap, counts, s)
-             : dispatch_epi<false, false>(p, a.epilogue, a.c_dtype, lists, cap, counts, s);
+  const int path = !dma ? 0 : (a.w_format == MOE_W_TILED ? 2 : 1);
+  if (fp8) return dispatch_path<true>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s);
+  return dispatch_path<false>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s);
 }
 
 }  // namespace mxmoe
