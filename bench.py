@@ -20,6 +20,7 @@ oracle runs here only in the CPU-baseline leg.
 from __future__ import annotations
 
 import argparse
+import dataclasses
 import hashlib
 import json
 import math
@@ -63,6 +64,8 @@ def parse():
     p.add_argument("--w-format", default=None, choices=["canonical", "tiled"],
                    help="weight order the GEMMs read (default: tiled at load time, untimed, when hidden "
                         "and intermediate are multiples of 512, else canonical)")
+    p.add_argument("--expert-copy", default="all", choices=["all", "routed", "auto"],
+                   help="streamed: move every expert per layer, or only the experts the layer's routing hits")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true", help="skip the output checks (profiling runs)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -426,6 +429,8 @@ def bench_graph(shape, w, x, xs, logits, inter, args, w_format="canonical"):
 
 def bench_streamed(args):
     shape = gen.preset("streamed")
+    if args.tokens:
+        shape = dataclasses.replace(shape, T=args.tokens)
     T, H, I, E, k, L = shape.T, shape.H, shape.I, shape.E, shape.k, shape.layers
     dev = "cuda"
     nbytes = mx.blob_bytes(H, I, E)
@@ -476,11 +481,15 @@ def bench_streamed(args):
         h2d.append(nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
     h2d_peak = max(h2d)
 
-    def run(depth, events=None):
+    def run(depth, events=None, expert_copy=args.expert_copy):
         nonlocal ws
         ws = mx.prefill_streamed(blobs, slots, logits, x, out, T=T, H=H, I=I, E=E, k=k, num_layers=L,
                                  layout=shape.layout, chain="rms", depth=depth, workspace=ws, events=events,
-                                 copy_stream=copy)
+                                 copy_stream=copy, expert_copy=expert_copy)
+
+    # experts each layer's routing hits (torch top-k over the logits: bytes accounting only)
+    hits = [int(torch.topk(logits[l], k, dim=1).indices.unique().numel()) if T else 0 for l in range(L)]
+    per_expert = 3 * H * I * 17 // 32
 
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(4 * L)]
     for e in ev:
@@ -507,8 +516,19 @@ def bench_streamed(args):
     b.record()
     torch.cuda.synchronize()
     ms1 = a.elapsed_time(b)
-    h2d_bytes = L * nbytes
+    routed = args.expert_copy == "routed"
+    h2d_bytes = sum(hits) * per_expert if routed else L * nbytes
     achieved = h2d_bytes / (ms * 1e-3) / 1e9
+    all_ms = None
+    if routed:
+        # the all-experts stream at the same T, for comparison
+        run(2, expert_copy="all")
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        run(2, expert_copy="all")
+        b.record()
+        torch.cuda.synchronize()
+        all_ms = a.elapsed_time(b)
     flops = gen.flops(shape) * L
     rec = {
         "metric": METRIC, "value": T / (ms * 1e-3), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps,
@@ -516,7 +536,9 @@ def bench_streamed(args):
         "vs_baseline": None, "dtype": "bf16xmxfp4", "data": "synthetic",
         "config": {"workload": "streamed", "layers": L, "T": T, "hidden": H, "intermediate": I, "experts": E,
                    "top_k": k, "distinct_host_blobs": n_blobs, "blob_GB": nbytes / 1e9,
-                   "parallelism": "none (1 GPU)"},
+                   "expert_copy": args.expert_copy, "parallelism": "none (1 GPU)"},
+        "experts_hit_per_layer_mean": float(np.mean(hits)), "h2d_bytes_per_pass": h2d_bytes,
+        "all_experts_ms": all_ms,
         "tflops": flops / (ms * 1e-3) / 1e12,
         "h2d_GBps": achieved, "h2d_measured_peak_GBps": h2d_peak, "h2d_frac_of_measured": achieved / h2d_peak,
         "serialized_ms": ms1, "serialized_tokens_per_s": T / (ms1 * 1e-3),

@@ -50,7 +50,7 @@
 extern "C" {
 #endif
 
-#define MXMOE_ABI_VERSION 2
+#define MXMOE_ABI_VERSION 3
 
 /* Every enum value is explicit and checked by the binding at load time:
  * a value that means one thing on one side of the boundary and another on
@@ -94,9 +94,15 @@ typedef enum moe_weight_format { /* how a weight matrix and its scales sit in me
   MOE_W_TILED = 1                /* the load-time tiling of moe_mxfp4_tile_weights */
 } moe_weight_format;
 
+typedef enum moe_expert_copy {   /* which experts the streamed prefill moves to HBM per layer */
+  MOE_COPY_ALL = 0,              /* every expert of the layer (one copy-engine transfer) */
+  MOE_COPY_ROUTED = 1,           /* only the experts the layer's routing hits (a copy kernel) */
+  MOE_COPY_AUTO = 2              /* ROUTED when T <= routed_copy_max_tokens, else ALL */
+} moe_expert_copy;
+
 typedef enum moe_enum_kind {
   MOE_ENUM_STATUS = 0, MOE_ENUM_ACT = 1, MOE_ENUM_OUT = 2, MOE_ENUM_EPI = 3, MOE_ENUM_CHAIN = 4,
-  MOE_ENUM_WFORMAT = 5
+  MOE_ENUM_WFORMAT = 5, MOE_ENUM_COPY = 6
 } moe_enum_kind;
 
 /* ------------------------------------------------------------ queries -- */
@@ -341,6 +347,10 @@ typedef struct moe_streamed_args {
   void*          workspace;      /* device, >= moe_streamed_workspace_size() */
   size_t         workspace_bytes;
   int32_t        w_format;       /* moe_weight_format of the blobs' W1/S1 and W2/S2 sections */
+  int32_t        expert_copy;    /* moe_expert_copy */
+  int32_t        routed_copy_max_tokens; /* MOE_COPY_AUTO: the largest T that copies routed
+                                    experts only (the token threshold below which a
+                                    layer's batch leaves most experts unused) */
 } moe_streamed_args;
 
 /* Bytes of one layer's weight blob, and the byte offset of its sections:
@@ -358,6 +368,19 @@ size_t     moe_streamed_workspace_size(int32_t T, int32_t H, int32_t I, int32_t 
  * stream's earlier work.  Nothing waits on the host; on return both
  * streams hold the whole pass and `out` is ordered on `compute`.
  * MOE_ERR_NOT_PINNED if a blob is not page-locked host memory.
+ *
+ * Routed expert copy (MOE_COPY_ROUTED, or MOE_COPY_AUTO with
+ * T <= routed_copy_max_tokens): the router logits of every layer are inputs
+ * of the call, so layer L's routing is known before layer L-1 ends.  The
+ * copy stream then routes and permutes layer L itself (into its own
+ * double-buffered routing arrays) and moves only the experts with at least
+ * one routed row, with a kernel that reads the blob through its
+ * device-mapped address (a blob that has none is MOE_ERR_NOT_PINNED); the
+ * compute stream runs FC1, FC2 and the combine on that routing.  The
+ * experts the layer does not hit keep whatever the slot held before: no
+ * kernel reads them.  The GEMMs then leave one CU per XCD free for the copy
+ * kernel.  Outputs are bitwise those of MOE_COPY_ALL.  Blob and slot
+ * addresses must be 16-byte aligned (MOE_ERR_INVALID_ARG otherwise).
  */
 moe_status moe_layer_prefill_streamed(const moe_streamed_args* args, void* compute_stream,
                                       void* copy_stream);

@@ -17,7 +17,7 @@ import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(_HERE, "libmxmoe.so")
-ABI_VERSION = 2
+ABI_VERSION = 3
 
 # mirrors of include/mxmoe.h; checked against the library at import
 STATUS = {"MOE_OK": 0, "MOE_ERR_INVALID_ARG": 1, "MOE_ERR_SHAPE": 2, "MOE_ERR_UNSUPPORTED_DEVICE": 3,
@@ -27,7 +27,9 @@ OUT = {"MOE_OUT_FP32": 0, "MOE_OUT_BF16": 1, "MOE_OUT_MXFP8_E4M3": 2}
 EPI = {"MOE_EPI_NONE": 0, "MOE_EPI_SWIGLU_SPLIT": 1, "MOE_EPI_SWIGLU_INTERLEAVED": 2}
 CHAIN = {"MOE_CHAIN_RMS": 0, "MOE_CHAIN_INDEPENDENT": 1}
 WFORMAT = {"MOE_W_CANONICAL": 0, "MOE_W_TILED": 1}
-ENUM_KINDS = {0: STATUS, 1: ACT, 2: OUT, 3: EPI, 4: CHAIN, 5: WFORMAT}
+COPY = {"MOE_COPY_ALL": 0, "MOE_COPY_ROUTED": 1, "MOE_COPY_AUTO": 2}
+ENUM_KINDS = {0: STATUS, 1: ACT, 2: OUT, 3: EPI, 4: CHAIN, 5: WFORMAT, 6: COPY}
+EXPERT_COPY = {"all": COPY["MOE_COPY_ALL"], "routed": COPY["MOE_COPY_ROUTED"], "auto": COPY["MOE_COPY_AUTO"]}
 W_FORMAT = {"canonical": WFORMAT["MOE_W_CANONICAL"], "tiled": WFORMAT["MOE_W_TILED"]}
 
 LAYOUT = {"split": EPI["MOE_EPI_SWIGLU_SPLIT"], "interleaved": EPI["MOE_EPI_SWIGLU_INTERLEAVED"]}
@@ -61,7 +63,8 @@ class StreamedArgs(ctypes.Structure):
                 ("layout", _i32), ("chain", _i32), ("depth", _i32), ("num_blobs", _i32),
                 ("host_blobs", ctypes.POINTER(_vp)), ("blob_bytes", _sz), ("device_slot", _vp * 2),
                 ("logits", _vp), ("x", _vp), ("out", _vp), ("layer_inputs", _vp), ("events", _vp),
-                ("workspace", _vp), ("workspace_bytes", _sz), ("w_format", _i32)]
+                ("workspace", _vp), ("workspace_bytes", _sz), ("w_format", _i32), ("expert_copy", _i32),
+                ("routed_copy_max_tokens", _i32)]
 
 
 def _load():
@@ -365,8 +368,13 @@ def prefill_streamed(host_blobs: Sequence[torch.Tensor], slots: Sequence[torch.T
                      x: torch.Tensor, out: torch.Tensor, *, T: int, H: int, I: int, E: int, k: int,
                      num_layers: int, layout: str = "split", chain: str = "rms", depth: int = 2,
                      layer_inputs: Optional[torch.Tensor] = None, events=None, workspace=None,
-                     compute_stream=None, copy_stream=None, w_format: str = "canonical"):
-    """moe_layer_prefill_streamed.  host_blobs: pinned uint8 CPU tensors (layer L uses blob L % n)."""
+                     compute_stream=None, copy_stream=None, w_format: str = "canonical",
+                     expert_copy: str = "all", routed_copy_max_tokens: int = 0):
+    """moe_layer_prefill_streamed.  host_blobs: pinned uint8 CPU tensors (layer L uses blob L % n).
+
+    expert_copy: "all" moves every expert of a layer, "routed" only the experts
+    its routing hits, "auto" routed when T <= routed_copy_max_tokens.
+    """
     nb = len(host_blobs)
     arr = (_vp * nb)(*[b.data_ptr() for b in host_blobs])
     need = lib.moe_streamed_workspace_size(T, H, I, E, k)
@@ -384,7 +392,8 @@ def prefill_streamed(host_blobs: Sequence[torch.Tensor], slots: Sequence[torch.T
                         layer_inputs=layer_inputs.data_ptr() if layer_inputs is not None else None,
                         events=ctypes.cast(ev_arr, _vp) if ev_arr is not None else None,
                         workspace=workspace.data_ptr(), workspace_bytes=workspace.numel(),
-                        w_format=W_FORMAT[w_format])
+                        w_format=W_FORMAT[w_format], expert_copy=EXPERT_COPY[expert_copy],
+                        routed_copy_max_tokens=routed_copy_max_tokens)
     cs = _stream(compute_stream)
     xs = _stream(copy_stream) if copy_stream is not None else cs
     _check(lib.moe_layer_prefill_streamed(ctypes.byref(args), cs, xs))

@@ -106,6 +106,10 @@ const char* moe_enum_name(int kind, int v) {
       return v == MOE_CHAIN_RMS ? "MOE_CHAIN_RMS" : v == MOE_CHAIN_INDEPENDENT ? "MOE_CHAIN_INDEPENDENT" : nullptr;
     case MOE_ENUM_WFORMAT:
       return v == MOE_W_CANONICAL ? "MOE_W_CANONICAL" : v == MOE_W_TILED ? "MOE_W_TILED" : nullptr;
+    case MOE_ENUM_COPY:
+      return v == MOE_COPY_ALL ? "MOE_COPY_ALL"
+             : v == MOE_COPY_ROUTED ? "MOE_COPY_ROUTED"
+             : v == MOE_COPY_AUTO ? "MOE_COPY_AUTO" : nullptr;
     default: return nullptr;
   }
 }

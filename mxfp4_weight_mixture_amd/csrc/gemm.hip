@@ -1251,9 +1251,17 @@ int class_grid() {
   return grid;
 }
 
+// `reserve`: CUs per XCD left without a block of this launch, so that a
+// kernel on another stream (the routed expert copy) finds a free CU beside a
+// persistent GEMM that otherwise fills every CU's LDS.
 template <int BM, bool FP8, int EPI, int OUT, int PATH>
-moe_status launch_class(const Params& p, hipStream_t s) {
-  const int grid = class_grid<BM, FP8, EPI, OUT, PATH>();
+moe_status launch_class(const Params& p, hipStream_t s, int reserve) {
+  int grid = class_grid<BM, FP8, EPI, OUT, PATH>();
+  if (reserve > 0) {
+    const int per_cu = grid / num_cus() > 0 ? grid / num_cus() : 1;
+    grid = (grid - reserve * kXcds * per_cu) / kXcds * kXcds;
+    if (grid < kXcds) grid = kXcds;
+  }
   if constexpr (PATH != 0)
     hipLaunchKernelGGL((gemm_dma_kernel<BM, FP8, EPI, OUT, PATH == 2>), dim3(grid),
                        dim3(64 * dma_waves<BM, FP8, EPI>()), 0, s, p);
@@ -1268,48 +1276,49 @@ moe_status launch_class(const Params& p, hipStream_t s) {
 // the CUs was measured slower: a few CUs cannot pull the weight stream at
 // HBM rate, and the full tiles lose those CUs for longer.)
 template <bool FP8, int EPI, int OUT, int PATH>
-moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* counts, hipStream_t s) {
+moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* counts, hipStream_t s,
+                      int reserve) {
   int32_t* const ctr = p.unit_ctr;
   auto at = [&](int c) {
     p.tiles = lists + c * cap;
     p.tile_count = counts + c;
     p.unit_ctr = ctr + c * kXcds;
   };
-  at(0); MXMOE_TRY((launch_class<32, FP8, EPI, OUT, PATH>(p, s)));
-  at(1); MXMOE_TRY((launch_class<64, FP8, EPI, OUT, PATH>(p, s)));
-  at(2); MXMOE_TRY((launch_class<128, FP8, EPI, OUT, PATH>(p, s)));
+  at(0); MXMOE_TRY((launch_class<32, FP8, EPI, OUT, PATH>(p, s, reserve)));
+  at(1); MXMOE_TRY((launch_class<64, FP8, EPI, OUT, PATH>(p, s, reserve)));
+  at(2); MXMOE_TRY((launch_class<128, FP8, EPI, OUT, PATH>(p, s, reserve)));
   // the bf16 DMA kernel's full tile is 128 rows (its 256-row stages do not fit
   // in LDS), so its class-3 list is empty
   if constexpr (!(PATH != 0 && !FP8)) {
-    at(3); MXMOE_TRY((launch_class<256, FP8, EPI, OUT, PATH>(p, s)));
+    at(3); MXMOE_TRY((launch_class<256, FP8, EPI, OUT, PATH>(p, s, reserve)));
   }
   return MOE_OK;
 }
 
 template <bool FP8, int EPI, int PATH>
 moe_status dispatch_out(const Params& p, int c_dtype, const Tile* lists, int cap,
-                        const int32_t* counts, hipStream_t s) {
-  if (c_dtype == MOE_OUT_FP32) return launch_all<FP8, EPI, MOE_OUT_FP32, PATH>(p, lists, cap, counts, s);
-  if (c_dtype == MOE_OUT_BF16) return launch_all<FP8, EPI, MOE_OUT_BF16, PATH>(p, lists, cap, counts, s);
+                        const int32_t* counts, hipStream_t s, int reserve) {
+  if (c_dtype == MOE_OUT_FP32) return launch_all<FP8, EPI, MOE_OUT_FP32, PATH>(p, lists, cap, counts, s, reserve);
+  if (c_dtype == MOE_OUT_BF16) return launch_all<FP8, EPI, MOE_OUT_BF16, PATH>(p, lists, cap, counts, s, reserve);
   if constexpr (PATH != 0 && EPI != 0)
-    return launch_all<FP8, EPI, MOE_OUT_MXFP8_E4M3, PATH>(p, lists, cap, counts, s);
+    return launch_all<FP8, EPI, MOE_OUT_MXFP8_E4M3, PATH>(p, lists, cap, counts, s, reserve);
   return fail(MOE_ERR_NOT_IMPLEMENTED,
               "grouped GEMM: MXFP8 output needs the SwiGLU epilogue and K %% 512 == 0");
 }
 
 template <bool FP8, int PATH>
 moe_status dispatch_epi(const Params& p, int epi, int c_dtype, const Tile* lists, int cap,
-                        const int32_t* counts, hipStream_t s) {
-  if (epi == MOE_EPI_NONE) return dispatch_out<FP8, 0, PATH>(p, c_dtype, lists, cap, counts, s);
-  return dispatch_out<FP8, 1, PATH>(p, c_dtype, lists, cap, counts, s);
+                        const int32_t* counts, hipStream_t s, int reserve) {
+  if (epi == MOE_EPI_NONE) return dispatch_out<FP8, 0, PATH>(p, c_dtype, lists, cap, counts, s, reserve);
+  return dispatch_out<FP8, 1, PATH>(p, c_dtype, lists, cap, counts, s, reserve);
 }
 
 template <bool FP8>
 moe_status dispatch_path(int path, const Params& p, int epi, int c_dtype, const Tile* lists, int cap,
-                         const int32_t* counts, hipStream_t s) {
-  if (path == 2) return dispatch_epi<FP8, 2>(p, epi, c_dtype, lists, cap, counts, s);
-  if (path == 1) return dispatch_epi<FP8, 1>(p, epi, c_dtype, lists, cap, counts, s);
-  return dispatch_epi<FP8, 0>(p, epi, c_dtype, lists, cap, counts, s);
+                         const int32_t* counts, hipStream_t s, int reserve) {
+  if (path == 2) return dispatch_epi<FP8, 2>(p, epi, c_dtype, lists, cap, counts, s, reserve);
+  if (path == 1) return dispatch_epi<FP8, 1>(p, epi, c_dtype, lists, cap, counts, s, reserve);
+  return dispatch_epi<FP8, 0>(p, epi, c_dtype, lists, cap, counts, s, reserve);
 }
 
 }  // namespace
@@ -1384,7 +1393,7 @@ moe_status launch_tile(const uint8_t* src_p, const uint8_t* src_s, int E, int N,
   return MOE_OK;
 }
 
-moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
+moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s, int reserve) {
   if (a.rows == 0) return MOE_OK;
   const int cap = list_capacity(a.rows, a.E);
   Tile* lists = static_cast<Tile*>(ws);
@@ -1422,8 +1431,8 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s) {
     p.n_tiles = (p.n_out + kBN / 2 - 1) / (kBN / 2);
   }
   const int path = !dma ? 0 : (a.w_format == MOE_W_TILED ? 2 : 1);
-  if (fp8) return dispatch_path<true>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s);
-  return dispatch_path<false>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s);
+  if (fp8) return dispatch_path<true>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s, reserve);
+  return dispatch_path<false>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s, reserve);
 }
 
 }  // namespace mxmoe

@@ -41,10 +41,16 @@ size_t permute_ws_bytes(int T, int E, int k);
 moe_status launch_permute(const int32_t* ids, int T, int E, int k, int32_t* off, int32_t* perm_src,
                           int32_t* dest_row, void* ws, hipStream_t s);
 size_t gemm_ws_bytes(int rows, int E);
-moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s);
+// reserve: CUs per XCD that the persistent GEMM launches leave free (0: none)
+moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s, int reserve = 0);
 moe_status launch_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* w,
                           int T, int k, int H, float* out, uint16_t* x_next, hipStream_t s);
 moe_status validate_gemm(const moe_gemm_args& a);
+// routed expert copy (expert_copy.hip): copies expert e's byte range of each of
+// the four sections when expert_offsets[e + 1] > expert_offsets[e]; `blocks`
+// blocks of 1024 threads
+moe_status launch_routed_copy(const uint8_t* const src[4], uint8_t* const dst[4], const uint64_t per_expert[4],
+                              const int32_t* expert_offsets, int E, int blocks, hipStream_t s);
 // load-time weight tiling (gemm.hip)
 bool tile_shape_ok(int E, int N, int K);
 size_t tiled_bytes(int E, int N, int K, int which);

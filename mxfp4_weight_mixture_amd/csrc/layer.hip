@@ -66,32 +66,87 @@ moe_status validate_w_format(int w_format, int H, int I) {
   return MOE_OK;
 }
 
-// The body of a layer, all arguments valid; pointers into `ws`.
-moe_status run_layer(const moe_layer_args& a, hipStream_t s) {
-  if (a.T == 0) return MOE_OK;
+// A layer's routing arrays (route + permute outputs) and the permutation's
+// scratch.
+struct Routing {
+  int32_t* ids;
+  float* w;
+  int32_t* off;
+  int32_t* perm_src;
+  int32_t* dest_row;
+  void* permute_ws;
+};
+
+Routing layer_routing(const LayerWs& L, uint8_t* ws) {
+  Routing r{};
+  r.ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  r.w = reinterpret_cast<float*>(ws + L.w);
+  r.off = reinterpret_cast<int32_t*>(ws + L.off);
+  r.perm_src = reinterpret_cast<int32_t*>(ws + L.perm_src);
+  r.dest_row = reinterpret_cast<int32_t*>(ws + L.dest_row);
+  r.permute_ws = ws + L.permute_ws;
+  return r;
+}
+
+// Routing arrays alone (the streamed pass's per-slot copies).
+struct RouteWs {
+  size_t ids, w, off, perm_src, dest_row, permute_ws, total;
+};
+
+RouteWs route_ws_layout(int T, int E, int k) {
+  RouteWs w{};
+  const size_t rows = (size_t)T * k;
+  size_t o = 0;
+  auto take = [&](size_t bytes) {
+    const size_t at = o;
+    o = align_up(o + bytes, 256);
+    return at;
+  };
+  w.ids = take(rows * 4);
+  w.w = take(rows * 4);
+  w.off = take(((size_t)E + 1) * 4);
+  w.perm_src = take(rows * 4);
+  w.dest_row = take(rows * 4);
+  w.permute_ws = take(permute_ws_bytes(T, E, k));
+  w.total = o;
+  return w;
+}
+
+Routing slot_routing(const RouteWs& L, uint8_t* ws) {
+  Routing r{};
+  r.ids = reinterpret_cast<int32_t*>(ws + L.ids);
+  r.w = reinterpret_cast<float*>(ws + L.w);
+  r.off = reinterpret_cast<int32_t*>(ws + L.off);
+  r.perm_src = reinterpret_cast<int32_t*>(ws + L.perm_src);
+  r.dest_row = reinterpret_cast<int32_t*>(ws + L.dest_row);
+  r.permute_ws = ws + L.permute_ws;
+  return r;
+}
+
+moe_status run_routing(const float* logits, int T, int E, int k, const Routing& r, hipStream_t s) {
+  MXMOE_TRY(launch_route(logits, T, E, k, r.ids, r.w, s));
+  return launch_permute(r.ids, T, E, k, r.off, r.perm_src, r.dest_row, r.permute_ws, s);
+}
+
+// FC1 + SwiGLU -> FC2 -> combine of a routed layer, all arguments valid, T > 0;
+// intermediate, FC2 output and GEMM scratch in a.workspace.  `reserve`: CUs
+// per XCD the GEMMs leave free.
+moe_status run_experts(const moe_layer_args& a, const Routing& r, hipStream_t s, int reserve) {
   const LayerWs L = layer_ws_layout(a.T, a.H, a.I, a.E, a.k, a.inter_dtype);
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
-  int32_t* ids = reinterpret_cast<int32_t*>(ws + L.ids);
-  float* w = reinterpret_cast<float*>(ws + L.w);
-  int32_t* off = reinterpret_cast<int32_t*>(ws + L.off);
-  int32_t* perm_src = reinterpret_cast<int32_t*>(ws + L.perm_src);
-  int32_t* dest_row = reinterpret_cast<int32_t*>(ws + L.dest_row);
   const int rows = a.T * a.k;
-
-  MXMOE_TRY(launch_route(a.logits, a.T, a.E, a.k, ids, w, s));
-  MXMOE_TRY(launch_permute(ids, a.T, a.E, a.k, off, perm_src, dest_row, ws + L.permute_ws, s));
 
   moe_gemm_args g1{};
   g1.a = a.x;
   g1.a_scales = a.x_scales;
   g1.a_dtype = a.act_dtype;
-  g1.a_gather = perm_src;
+  g1.a_gather = r.perm_src;
   g1.a_gather_div = a.k;
   g1.a_rows = a.T;
   g1.rows = rows;
   g1.w_packed = a.w1_packed;
   g1.w_scales = a.w1_scales;
-  g1.expert_offsets = off;
+  g1.expert_offsets = r.off;
   g1.E = a.E;
   g1.N = 2 * a.I;
   g1.K = a.H;
@@ -100,7 +155,7 @@ moe_status run_layer(const moe_layer_args& a, hipStream_t s) {
   g1.c_scales = a.inter_dtype == MOE_OUT_MXFP8_E4M3 ? ws + L.inter_scales : nullptr;
   g1.c_dtype = a.inter_dtype;
   g1.w_format = a.w_format;
-  MXMOE_TRY(launch_gemm(g1, ws + L.gemm_ws, s));
+  MXMOE_TRY(launch_gemm(g1, ws + L.gemm_ws, s, reserve));
 
   moe_gemm_args g2{};
   g2.a = ws + L.inter;
@@ -112,7 +167,7 @@ moe_status run_layer(const moe_layer_args& a, hipStream_t s) {
   g2.rows = rows;
   g2.w_packed = a.w2_packed;
   g2.w_scales = a.w2_scales;
-  g2.expert_offsets = off;
+  g2.expert_offsets = r.off;
   g2.E = a.E;
   g2.N = a.H;
   g2.K = a.I;
@@ -120,9 +175,18 @@ moe_status run_layer(const moe_layer_args& a, hipStream_t s) {
   g2.c = ws + L.y;
   g2.c_dtype = MOE_OUT_BF16;
   g2.w_format = a.w_format;
-  MXMOE_TRY(launch_gemm(g2, ws + L.gemm_ws, s));
+  MXMOE_TRY(launch_gemm(g2, ws + L.gemm_ws, s, reserve));
 
-  return launch_combine(ws + L.y, MOE_OUT_BF16, dest_row, w, a.T, a.k, a.H, a.out, a.x_next, s);
+  return launch_combine(ws + L.y, MOE_OUT_BF16, r.dest_row, r.w, a.T, a.k, a.H, a.out, a.x_next, s);
+}
+
+// The body of a layer, all arguments valid; pointers into `ws`.
+moe_status run_layer(const moe_layer_args& a, hipStream_t s) {
+  if (a.T == 0) return MOE_OK;
+  const LayerWs L = layer_ws_layout(a.T, a.H, a.I, a.E, a.k, a.inter_dtype);
+  const Routing r = layer_routing(L, static_cast<uint8_t*>(a.workspace));
+  MXMOE_TRY(run_routing(a.logits, a.T, a.E, a.k, r, s));
+  return run_experts(a, r, s, 0);
 }
 
 struct BlobLayout {
@@ -141,8 +205,11 @@ BlobLayout blob_layout(int H, int I, int E) {
   return b;
 }
 
+// Streamed-pass workspace: one layer workspace, the fp32 output of inner
+// layers, two bf16 chain buffers, and per slot the routing arrays of the
+// routed expert copy (laid out as the routing part of a layer workspace).
 struct StreamWs {
-  size_t layer, out_tmp, xbuf0, xbuf1, total;
+  size_t layer, out_tmp, xbuf0, xbuf1, route[2], route_bytes, total;
 };
 
 StreamWs stream_ws_layout(int T, int H, int I, int E, int k) {
@@ -157,6 +224,9 @@ StreamWs stream_ws_layout(int T, int H, int I, int E, int k) {
   s.out_tmp = take((size_t)T * H * 4);
   s.xbuf0 = take((size_t)T * H * 2);
   s.xbuf1 = take((size_t)T * H * 2);
+  s.route_bytes = route_ws_layout(T, E, k).total;
+  s.route[0] = take(s.route_bytes);
+  s.route[1] = take(s.route_bytes);
   s.total = o;
   return s;
 }
@@ -254,6 +324,12 @@ moe_status moe_layer_prefill_streamed(const moe_streamed_args* a, void* compute_
   if (a->depth != 1 && a->depth != 2) return fail(MOE_ERR_INVALID_ARG, "streamed: depth %d must be 1 or 2", a->depth);
   if (a->chain != MOE_CHAIN_RMS && a->chain != MOE_CHAIN_INDEPENDENT)
     return fail(MOE_ERR_INVALID_ARG, "streamed: bad chain %d", a->chain);
+  if (a->expert_copy != MOE_COPY_ALL && a->expert_copy != MOE_COPY_ROUTED && a->expert_copy != MOE_COPY_AUTO)
+    return fail(MOE_ERR_INVALID_ARG, "streamed: bad expert_copy %d", a->expert_copy);
+  if (a->routed_copy_max_tokens < 0)
+    return fail(MOE_ERR_INVALID_ARG, "streamed: routed_copy_max_tokens %d < 0", a->routed_copy_max_tokens);
+  const bool routed = a->expert_copy == MOE_COPY_ROUTED ||
+                      (a->expert_copy == MOE_COPY_AUTO && a->T <= a->routed_copy_max_tokens);
   if (a->num_blobs < 1 || !a->host_blobs) return fail(MOE_ERR_INVALID_ARG, "streamed: no host blobs");
   if (!a->device_slot[0] || (a->depth == 2 && !a->device_slot[1]))
     return fail(MOE_ERR_INVALID_ARG, "streamed: device slot missing");
@@ -266,14 +342,27 @@ moe_status moe_layer_prefill_streamed(const moe_streamed_args* a, void* compute_
     return fail(MOE_ERR_WORKSPACE, "streamed: workspace %zu bytes, need %zu", a->workspace_bytes, sw.total);
   for (int b = 0; b < a->num_blobs; ++b) {
     if (!a->host_blobs[b]) return fail(MOE_ERR_INVALID_ARG, "streamed: host blob %d is null", b);
+    if (routed && reinterpret_cast<uintptr_t>(a->host_blobs[b]) % 16)
+      return fail(MOE_ERR_INVALID_ARG, "streamed: routed copy needs 16-byte aligned blobs (blob %d)", b);
   }
+  for (int i = 0; i < a->depth; ++i)
+    if (routed && reinterpret_cast<uintptr_t>(a->device_slot[i]) % 16)
+      return fail(MOE_ERR_INVALID_ARG, "streamed: routed copy needs 16-byte aligned slots (slot %d)", i);
   MXMOE_TRY(check_device());
+  // the routed copy kernel reads each blob through the address the device
+  // maps it at
+  std::vector<const uint8_t*> dev_blob(a->num_blobs, nullptr);
   for (int b = 0; b < a->num_blobs; ++b) {
     hipPointerAttribute_t attr;
     const hipError_t e = hipPointerGetAttributes(&attr, a->host_blobs[b]);
     (void)hipGetLastError();
     if (e != hipSuccess || attr.type != hipMemoryTypeHost)
       return fail(MOE_ERR_NOT_PINNED, "streamed: host blob %d is not page-locked host memory", b);
+    if (routed) {
+      if (!attr.devicePointer || attr.hostPointer != a->host_blobs[b])
+        return fail(MOE_ERR_NOT_PINNED, "streamed: host blob %d has no device-mapped address", b);
+      dev_blob[b] = static_cast<const uint8_t*>(attr.devicePointer);
+    }
   }
 
   hipStream_t cs = (hipStream_t)compute_stream, xs = (hipStream_t)copy_stream;
@@ -286,6 +375,16 @@ moe_status moe_layer_prefill_streamed(const moe_streamed_args* a, void* compute_
 
   uint8_t* ws = static_cast<uint8_t*>(a->workspace);
   const size_t TH = (size_t)a->T * a->H;
+  const RouteWs rw = route_ws_layout(a->T, a->E, a->k);
+  const Routing slot_route[2] = {slot_routing(rw, ws + sw.route[0]), slot_routing(rw, ws + sw.route[1])};
+  // bytes of one expert in each blob section (contiguous per expert in both weight orders)
+  const uint64_t per_expert[4] = {(uint64_t)2 * a->I * (a->H / 2), (uint64_t)2 * a->I * (a->H / 32),
+                                  (uint64_t)a->H * (a->I / 2), (uint64_t)a->H * (a->I / 32)};
+  const size_t sec[4] = {bl.w1p, bl.s1, bl.w2p, bl.s2};
+  // GEMMs leave one CU per XCD to the copy kernel, which runs one block per XCD
+  const int reserve = routed ? 1 : 0;
+  constexpr int kCopyBlocks = 8;
+
   // the copy stream must not overwrite a slot an earlier call's compute still reads
   MXMOE_HIP(hipEventRecord(start, cs));
   MXMOE_HIP(hipStreamWaitEvent(xs, start, 0));
@@ -294,12 +393,26 @@ moe_status moe_layer_prefill_streamed(const moe_streamed_args* a, void* compute_
   for (int L = 0; L < a->num_layers; ++L) {
     const int slot = a->depth == 2 ? (L & 1) : 0;
     uint8_t* dst = static_cast<uint8_t*>(a->device_slot[slot]);
-    const void* src = a->host_blobs[L % a->num_blobs];
+    const float* logits = a->logits + (size_t)L * a->T * a->E;
     // slot reuse: depth 2 waits for layer L-2, depth 1 for layer L-1
     const int prev = L - a->depth;
     if (prev >= 0) MXMOE_HIP(hipStreamWaitEvent(xs, computed[slot], 0));
     if (user_ev) MXMOE_HIP(hipEventRecord(user_ev[4 * L + 0], xs));
-    MXMOE_HIP(hipMemcpyAsync(dst, src, bl.total, hipMemcpyHostToDevice, xs));
+    if (routed) {
+      // this layer's routing on the copy stream, then only its hit experts
+      if (a->T > 0) {
+        MXMOE_TRY(run_routing(logits, a->T, a->E, a->k, slot_route[slot], xs));
+        const uint8_t* src[4];
+        uint8_t* dsts[4];
+        for (int i = 0; i < 4; ++i) {
+          src[i] = dev_blob[L % a->num_blobs] + sec[i];
+          dsts[i] = dst + sec[i];
+        }
+        MXMOE_TRY(launch_routed_copy(src, dsts, per_expert, slot_route[slot].off, a->E, kCopyBlocks, xs));
+      }
+    } else {
+      MXMOE_HIP(hipMemcpyAsync(dst, a->host_blobs[L % a->num_blobs], bl.total, hipMemcpyHostToDevice, xs));
+    }
     if (user_ev) MXMOE_HIP(hipEventRecord(user_ev[4 * L + 1], xs));
     MXMOE_HIP(hipEventRecord(copied[slot], xs));
 
@@ -318,7 +431,7 @@ moe_status moe_layer_prefill_streamed(const moe_streamed_args* a, void* compute_
     la.layout = a->layout;
     la.act_dtype = MOE_ACT_BF16;
     la.inter_dtype = MOE_OUT_BF16;
-    la.logits = a->logits + (size_t)L * a->T * a->E;
+    la.logits = logits;
     la.x = x_cur;
     la.x_scales = nullptr;
     la.w1_packed = dst + bl.w1p;
@@ -330,7 +443,11 @@ moe_status moe_layer_prefill_streamed(const moe_streamed_args* a, void* compute_
     la.workspace = ws + sw.layer;
     la.workspace_bytes = sw.out_tmp - sw.layer;
     la.w_format = a->w_format;
-    MXMOE_TRY(run_layer(la, cs));
+    if (routed) {
+      if (a->T > 0) MXMOE_TRY(run_experts(la, slot_route[slot], cs, reserve));
+    } else {
+      MXMOE_TRY(run_layer(la, cs));
+    }
     if (user_ev) MXMOE_HIP(hipEventRecord(user_ev[4 * L + 3], cs));
     MXMOE_HIP(hipEventRecord(computed[slot], cs));
     if (a->chain == MOE_CHAIN_RMS && !last) x_cur = x_next;

@@ -32,7 +32,7 @@ def test_every_declared_function_is_exported():
 
 
 def test_abi_version_and_enum_names():
-    assert mx.lib.moe_abi_version() == mx.ABI_VERSION == 2
+    assert mx.lib.moe_abi_version() == mx.ABI_VERSION == 3
     # each enum value round-trips through the library's names (the binding checked it at import too)
     for kind, table in mx.ENUM_KINDS.items():
         for name, value in table.items():
@@ -112,6 +112,25 @@ def test_streamed_argument_errors():
     args = mx.StreamedArgs(num_layers=2, T=4, H=128, I=64, E=4, k=2, layout=1, chain=0, depth=3, num_blobs=1)
     st, msg = _status(mx.lib.moe_layer_prefill_streamed(ctypes.byref(args), None, None))
     assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "depth" in msg
+    args = mx.StreamedArgs(num_layers=2, T=4, H=128, I=64, E=4, k=2, layout=1, chain=0, depth=2, num_blobs=1,
+                           expert_copy=3)
+    st, msg = _status(mx.lib.moe_layer_prefill_streamed(ctypes.byref(args), None, None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "expert_copy" in msg
+    args = mx.StreamedArgs(num_layers=2, T=4, H=128, I=64, E=4, k=2, layout=1, chain=0, depth=2, num_blobs=1,
+                           expert_copy=mx.COPY["MOE_COPY_AUTO"], routed_copy_max_tokens=-1)
+    st, msg = _status(mx.lib.moe_layer_prefill_streamed(ctypes.byref(args), None, None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "routed_copy_max_tokens" in msg
+
+
+def test_routed_copy_rejects_misaligned_blobs_before_any_device_call():
+    blob = (ctypes.c_uint8 * 4096)()
+    ptrs = (ctypes.c_void_p * 1)(ctypes.addressof(blob) + 8)
+    slots = (ctypes.c_void_p * 2)(256, 512)
+    args = mx.StreamedArgs(num_layers=1, T=4, H=128, I=64, E=4, k=2, layout=1, chain=0, depth=2, num_blobs=1,
+                           host_blobs=ptrs, blob_bytes=1 << 20, device_slot=slots, logits=256, x=256, out=256,
+                           workspace=256, workspace_bytes=1 << 30, expert_copy=mx.COPY["MOE_COPY_ROUTED"])
+    st, msg = _status(mx.lib.moe_layer_prefill_streamed(ctypes.byref(args), None, None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "16-byte aligned blobs" in msg
 
 
 def test_blob_layout_sections_are_aligned_and_ordered():
