@@ -10,22 +10,29 @@
 namespace mxmoe {
 namespace {
 
-__device__ inline void load8(const uint16_t* p, float* v) {
-  const uint4 q = *reinterpret_cast<const uint4*>(p);
-  const uint32_t u[4] = {q.x, q.y, q.z, q.w};
+// raw 8-element vectors: bf16 as one 16-byte load, fp32 as two
+struct Raw8Bf16 { uint4 q; };
+struct Raw8F32 { float4 a, b; };
+
+__device__ inline Raw8Bf16 load_raw(const uint16_t* p) { return {*reinterpret_cast<const uint4*>(p)}; }
+__device__ inline Raw8F32 load_raw(const float* p) {
+  return {*reinterpret_cast<const float4*>(p), *reinterpret_cast<const float4*>(p + 4)};
+}
+
+__device__ inline void widen(const Raw8Bf16& r, float* v) {
+  const uint32_t u[4] = {r.q.x, r.q.y, r.q.z, r.q.w};
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     v[2 * i] = __uint_as_float(u[i] << 16);
     v[2 * i + 1] = __uint_as_float(u[i] & 0xffff0000u);
   }
 }
-
-__device__ inline void load8(const float* p, float* v) {
-  const float4 a = *reinterpret_cast<const float4*>(p);
-  const float4 b = *reinterpret_cast<const float4*>(p + 4);
-  v[0] = a.x; v[1] = a.y; v[2] = a.z; v[3] = a.w;
-  v[4] = b.x; v[5] = b.y; v[6] = b.z; v[7] = b.w;
+__device__ inline void widen(const Raw8F32& r, float* v) {
+  v[0] = r.a.x; v[1] = r.a.y; v[2] = r.a.z; v[3] = r.a.w;
+  v[4] = r.b.x; v[5] = r.b.y; v[6] = r.b.z; v[7] = r.b.w;
 }
+
+__device__ inline void load8(const float* p, float* v) { widen(load_raw(p), v); }
 
 __device__ inline uint32_t bf16_rne(float f) {
   const uint32_t b = __float_as_uint(f);
@@ -33,25 +40,40 @@ __device__ inline uint32_t bf16_rne(float f) {
   return (b + 0x7fffu + ((b >> 16) & 1u)) >> 16;
 }
 
+// Rows are fetched kBatch at a time before any is accumulated (more loads in
+// flight per thread); the accumulation order stays j = 0, 1, ..., k-1.
+constexpr int kBatch = 8;
+
 template <typename YT>
 __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
                                                       const int32_t* __restrict__ dest_row,
                                                       const float* __restrict__ w, int k, int H,
                                                       float* __restrict__ out,
                                                       uint16_t* __restrict__ x_next) {
+  using Raw = decltype(load_raw(y));
   const int t = blockIdx.x;
   const int nv = H / 8;
   float* orow = out + (size_t)t * H;
+  const int32_t* rows = dest_row + (size_t)t * k;
+  const float* wt = w + (size_t)t * k;
   float ss = 0.f;
   for (int v = threadIdx.x; v < nv; v += 256) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-    for (int j = 0; j < k; ++j) {
-      const int r = dest_row[(size_t)t * k + j];
-      const float wj = w[(size_t)t * k + j];
-      float yv[8];
-      load8(y + (size_t)r * H + 8 * v, yv);
+    for (int j0 = 0; j0 < k; j0 += kBatch) {
+      Raw raw[kBatch];
 #pragma unroll
-      for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, yv[i], acc[i]);
+      for (int b = 0; b < kBatch; ++b)
+        if (j0 + b < k) raw[b] = load_raw(y + (size_t)rows[j0 + b] * H + 8 * v);
+#pragma unroll
+      for (int b = 0; b < kBatch; ++b) {
+        if (j0 + b < k) {
+          const float wj = wt[j0 + b];
+          float yv[8];
+          widen(raw[b], yv);
+#pragma unroll
+          for (int i = 0; i < 8; ++i) acc[i] = fmaf(wj, yv[i], acc[i]);
+        }
+      }
     }
     *reinterpret_cast<float4*>(orow + 8 * v) = make_float4(acc[0], acc[1], acc[2], acc[3]);
     *reinterpret_cast<float4*>(orow + 8 * v + 4) = make_float4(acc[4], acc[5], acc[6], acc[7]);

@@ -5,11 +5,15 @@
 //
 //   1. histogram: one workgroup per chunk of kChunk flat entries counts its
 //      experts in an LDS histogram (LDS atomics: order-free counts);
-//   2. scan: one workgroup turns the [chunk][expert] counts into each
-//      chunk's first row per expert (expert-major exclusive prefix), and
-//      writes expert_offsets;
-//   3. scatter: one wavefront per chunk walks its entries 64 at a time in
-//      order.  Lanes holding the same expert are grouped with a ballot;
+//   2. column scan: one wavefront per expert turns that expert's counts
+//      over the chunks into each chunk's first row relative to the expert
+//      (exclusive prefix, 64 chunks per step) and the expert's total;
+//   3. scatter: one wavefront per chunk first scans the experts' totals
+//      (every chunk needs the expert offsets; chunk 0 also writes them),
+//      then walks its entries 64 at a time in order.  Lanes holding the
+//      same expert are found with one ballot per bit of the expert id (the
+//      AND over the bits of "lanes whose bit agrees with mine"), so a step
+//      costs the same however many distinct experts its 64 entries hold;
 //      each lane's rank is the popcount of same-expert lanes below it, so
 //      ties keep flat-index order without any global atomics.
 #include "internal.h"
@@ -34,88 +38,78 @@ __global__ __launch_bounds__(256) void hist_kernel(const int32_t* __restrict__ i
   for (int e = threadIdx.x; e < E; e += 256) out[e] = hist[e];
 }
 
-// inclusive scan over a 1024-thread block
-__device__ inline int block_inclusive_scan(int v, int* wave_tot) {
-  const int lane = threadIdx.x & 63, wid = threadIdx.x >> 6;
+__device__ inline int wave_inclusive_scan(int v, int lane) {
 #pragma unroll
   for (int off = 1; off < 64; off <<= 1) {
     const int o = __shfl_up(v, off, 64);
     if (lane >= off) v += o;
   }
-  if (lane == 63) wave_tot[wid] = v;
-  __syncthreads();
-  if (wid == 0) {
-    int t = lane < 16 ? wave_tot[lane] : 0;
-#pragma unroll
-    for (int off = 1; off < 16; off <<= 1) {
-      const int o = __shfl_up(t, off, 64);
-      if (lane >= off) t += o;
-    }
-    if (lane < 16) wave_tot[lane] = t;
-  }
-  __syncthreads();
-  const int r = v + (wid > 0 ? wave_tot[wid - 1] : 0);
-  __syncthreads();
-  return r;
+  return v;
 }
 
-__global__ __launch_bounds__(1024) void scan_kernel(int32_t* __restrict__ counts, int nchunks,
-                                                    int E, int32_t* __restrict__ offsets) {
-  __shared__ int wave_tot[16];
-  __shared__ int carry;
-  if (threadIdx.x == 0) carry = 0;
-  __syncthreads();
-  for (int e0 = 0; e0 < E; e0 += 1024) {
-    const int e = e0 + threadIdx.x;
-    int tot = 0;
-    if (e < E)
-      for (int c = 0; c < nchunks; ++c) tot += counts[(size_t)c * E + e];
-    const int incl = block_inclusive_scan(tot, wave_tot);
-    const int base = carry + incl - tot;
-    if (e < E) {
-      offsets[e] = base;
-      int run = base;
-      for (int c = 0; c < nchunks; ++c) {
-        const size_t i = (size_t)c * E + e;
-        const int v = counts[i];
-        counts[i] = run;
-        run += v;
-      }
-    }
-    __syncthreads();
-    if (threadIdx.x == 1023) carry += incl;
-    __syncthreads();
+// counts[c][e] -> sum_{c' < c} counts[c'][e]; totals[e] = sum over all chunks
+__global__ __launch_bounds__(256) void colscan_kernel(int32_t* __restrict__ counts, int nchunks, int E,
+                                                      int32_t* __restrict__ totals) {
+  const int lane = threadIdx.x & 63;
+  const int e = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (e >= E) return;  // whole wave
+  int carry = 0;
+  for (int c0 = 0; c0 < nchunks; c0 += 64) {
+    const int c = c0 + lane;
+    const int v = c < nchunks ? counts[(size_t)c * E + e] : 0;
+    const int incl = wave_inclusive_scan(v, lane);
+    if (c < nchunks) counts[(size_t)c * E + e] = carry + incl - v;
+    carry += __shfl(incl, 63, 64);
   }
-  if (threadIdx.x == 0) offsets[E] = carry;
+  if (lane == 0) totals[e] = carry;
 }
 
-__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int n, int E,
+// nchunks == 0 runs one block that only writes the (zero) offsets
+__global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__ ids, int n, int E, int nbits,
                                                      const int32_t* __restrict__ chunk_first,
+                                                     const int32_t* __restrict__ totals,
+                                                     int32_t* __restrict__ offsets,
                                                      int32_t* __restrict__ perm_src,
                                                      int32_t* __restrict__ dest_row) {
   extern __shared__ int pos[];
   const int lane = threadIdx.x;
+  const bool has_entries = n > 0;
   const int32_t* first = chunk_first + (size_t)blockIdx.x * E;
-  for (int e = lane; e < E; e += 64) pos[e] = first[e];
+  int carry = 0;
+  for (int e0 = 0; e0 < E; e0 += 64) {
+    const int e = e0 + lane;
+    const int v = e < E ? totals[e] : 0;
+    const int incl = wave_inclusive_scan(v, lane);
+    if (e < E) {
+      const int start = carry + incl - v;
+      if (has_entries) pos[e] = start + first[e];
+      if (blockIdx.x == 0) offsets[e] = start;
+    }
+    carry += __shfl(incl, 63, 64);
+  }
+  if (blockIdx.x == 0 && lane == 0) offsets[E] = carry;
+  if (!has_entries) return;
   __syncthreads();
+  const uint64_t below = (1ull << lane) - 1ull;
   const int base = blockIdx.x * kChunk;
   for (int s = 0; s < kChunk; s += 64) {
     const int f = base + s + lane;
     const bool valid = f < n;
-    const int e = valid ? ids[f] : -1;
-    uint64_t pending = __ballot(valid);
-    while (pending) {
-      const int leader = __ffsll((unsigned long long)pending) - 1;
-      const int le = __shfl(e, leader, 64);
-      const uint64_t same = __ballot(e == le);
-      const int p0 = pos[le];  // wave-uniform address
-      if (e == le) {
-        const int row = p0 + __popcll(same & ((1ull << lane) - 1ull));
-        perm_src[row] = f;
-        dest_row[f] = row;
-      }
-      if (lane == leader) pos[le] = p0 + __popcll(same);
-      pending &= ~same;
+    const int e = valid ? ids[f] : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    // one LDS read per lane, then the lowest lane of each expert advances
+    // that expert's position (a wave's LDS operations complete in order)
+    const int p0 = valid ? pos[e] : 0;
+    if (valid) {
+      const int row = p0 + __popcll(same & below);
+      perm_src[row] = f;
+      dest_row[f] = row;
+      if ((same & below) == 0) pos[e] = p0 + __popcll(same);
     }
   }
 }
@@ -125,7 +119,7 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
 size_t permute_ws_bytes(int T, int E, int k) {
   const size_t n = (size_t)T * k;
   const size_t nchunks = (n + kChunk - 1) / kChunk;
-  return align_up(nchunks * (size_t)E * sizeof(int32_t), 256) + 256;
+  return align_up(nchunks * (size_t)E * sizeof(int32_t), 256) + align_up((size_t)E * sizeof(int32_t), 256);
 }
 
 moe_status launch_permute(const int32_t* ids, int T, int E, int k, int32_t* off,
@@ -133,18 +127,20 @@ moe_status launch_permute(const int32_t* ids, int T, int E, int k, int32_t* off,
   const int n = T * k;
   const int nchunks = (n + kChunk - 1) / kChunk;
   int32_t* counts = static_cast<int32_t*>(ws);
+  int32_t* totals = reinterpret_cast<int32_t*>(static_cast<uint8_t*>(ws) +
+                                               align_up((size_t)nchunks * E * sizeof(int32_t), 256));
   const size_t lds = (size_t)E * sizeof(int);
+  int nbits = 0;
+  while ((1 << nbits) < E) ++nbits;
   if (nchunks > 0) {
     hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), lds, s, ids, n, E, counts);
     MXMOE_HIP(hipGetLastError());
   }
-  hipLaunchKernelGGL(scan_kernel, dim3(1), dim3(1024), 0, s, counts, nchunks, E, off);
+  hipLaunchKernelGGL(colscan_kernel, dim3((E + 3) / 4), dim3(256), 0, s, counts, nchunks, E, totals);
   MXMOE_HIP(hipGetLastError());
-  if (nchunks > 0) {
-    hipLaunchKernelGGL(scatter_kernel, dim3(nchunks), dim3(64), lds, s, ids, n, E, counts, perm_src,
-                       dest_row);
-    MXMOE_HIP(hipGetLastError());
-  }
+  hipLaunchKernelGGL(scatter_kernel, dim3(nchunks > 0 ? nchunks : 1), dim3(64), lds, s, ids, n, E, nbits, counts,
+                     totals, off, perm_src, dest_row);
+  MXMOE_HIP(hipGetLastError());
   return MOE_OK;
 }
 

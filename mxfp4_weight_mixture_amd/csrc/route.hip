@@ -28,6 +28,12 @@ __device__ inline uint32_t order_key(float v) {
   return (b & 0x80000000u) ? ~b : (b | 0x80000000u);
 }
 
+// Inverse of order_key: the logit back from its key (-0 comes back as +0 and a
+// NaN as a NaN, which give the same weights).
+__device__ inline float key_value(uint32_t key) {
+  return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
+}
+
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) {
@@ -60,7 +66,7 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   }
 
   int my_id = 0;
-  float my_val = 0.f;
+  uint32_t my_key = 0u;
   for (int j = 0; j < k; ++j) {
     uint64_t best = 0ull;
 #pragma unroll
@@ -73,9 +79,11 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
     const int e = (int)(0xffffffffu - (uint32_t)(win & 0xffffffffu));
     if (lane == j) {
       my_id = e;
-      my_val = row[e];
+      my_key = (uint32_t)(win >> 32);
     }
   }
+  // the value from the key: no dependent global load per round
+  const float my_val = key_value(my_key);
   // max over all E is the first pick (NaN sorts last)
   const float m = __shfl(my_val, 0, 64);
   // exp(l_j - max) with the difference formed exactly in double

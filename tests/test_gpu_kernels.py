@@ -88,6 +88,17 @@ def test_permute_skewed_full_size_and_degenerate():
     assert off.cpu().tolist() == [0] * 7 and ps.numel() == 0
 
 
+@pytest.mark.parametrize("T,E,k,seed", [
+    (9000, 8192, 8, 0),      # the largest E (13 id bits), 71 chunks: the column scan carries across 64
+    (1500, 1024, 4, 1),      # ids with bit 9 set next to the last chunk's unused lanes
+    (70000, 3, 2, 2),        # 137 chunks, few experts: long same-expert runs in every 64 entries
+])
+def test_permute_uniform_ids_many_chunks(T, E, k, seed):
+    g = np.random.default_rng(seed)
+    ids = g.integers(0, E, (T, k), dtype=np.int32)    # repeats within a token are allowed here
+    _perm_check(ids, E)
+
+
 # ------------------------------------------------------ grouped GEMM
 
 def _rand_w(E, N, K, seed, lo=121, hi=127):
