@@ -25,6 +25,7 @@ import hashlib
 import json
 import math
 import os
+import re
 import sys
 import time
 
@@ -66,6 +67,9 @@ def parse():
                         "and intermediate are multiples of 512, else canonical)")
     p.add_argument("--expert-copy", default="all", choices=["all", "routed", "auto"],
                    help="streamed: move every expert per layer, or only the experts the layer's routing hits")
+    p.add_argument("--traffic-record", default=None, metavar="DIR",
+                   help="write profiles/gemm_traffic_<workload>.json from the rocprofv3 counter runs under DIR "
+                        "(subfolders pmc_FETCH_SIZE, pmc_WRITE_SIZE, cal_FETCH_SIZE, cal_WRITE_SIZE); no GPU needed")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--no-parity", action="store_true", help="skip the output checks (profiling runs)")
     p.add_argument("--copy-calibration", action="store_true",
@@ -346,7 +350,7 @@ def bench_layer(args):
                 "traffic": None, "kernel": f"{dom} grouped GEMM", "per_launch_ms": dm,
                 "algorithmic_per_launch": dfl}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(name, inter, dom, w_format)
+    roof["traffic"] = measured_traffic(name, inter, dom, w_format, T)
     rec = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -378,15 +382,80 @@ def bench_layer(args):
     return rec, shape, li, ids
 
 
-def measured_traffic(workload, inter, call, w_format):
+def _counter_rows(d):
+    """{kernel name: [counter value per dispatch]} of a rocprofv3 csv counter collection with one counter."""
+    import csv
+    import glob
+    files = sorted(glob.glob(os.path.join(d, "**", "*counter_collection.csv"), recursive=True))
+    if not files:
+        raise SystemExit(f"no *counter_collection.csv under {d}")
+    per = {}
+    for f in files:
+        for r in csv.DictReader(open(f)):
+            per.setdefault(r["Kernel_Name"], []).append(float(r["Counter_Value"]))
+    return per
+
+
+def _gemm_call(kernel_name):
+    """'fc1' / 'fc2' for a grouped-GEMM class kernel (epilogue template argument 1 / 0), else None."""
+    for tag in ("gemm_dma_kernel<", "gemm_kernel<"):
+        if tag in kernel_name:
+            targs = kernel_name.split(tag, 1)[1].split(">", 1)[0].split(",")
+            return "fc1" if int(targs[2]) != 0 else "fc2"
+    return None
+
+
+def write_traffic_record(args):
+    """HBM bytes per FC1 / FC2 call from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by
+    what the same counter reads for a device add of 1 GiB in and 1 GiB out (bench.py --copy-calibration).
+    A call is one launch per row-tile class, so a call's bytes are the sum of the class kernels' means."""
+    name = args.workload
+    shape = gen.preset(name, **({"T": args.tokens} if args.tokens else {}))
+    inter = args.inter or ("mxfp8" if shape.act == "mxfp8" and shape.H % 512 == 0 else "bf16")
+    w_format = args.w_format or ("tiled" if shape.H % 512 == 0 and shape.I % 512 == 0 else "canonical")
+    d = args.traffic_record
+    scale = {}
+    for ctr in ("FETCH_SIZE", "WRITE_SIZE"):
+        # the add dispatches only (the fill that makes the source reads nothing)
+        cal = [v for k, vals in _counter_rows(os.path.join(d, f"cal_{ctr}")).items()
+               if "elementwise" in k and "_add" in k for v in vals]
+        scale[ctr] = (1 << 30) / 1024 / float(np.mean(cal))
+    rec = {"workload": name, "T": shape.T, "intermediate_dtype": inter, "weight_format": w_format,
+           "gemm_source_sha256": hashlib.sha256(open(os.path.join(ROOT, "mxfp4_weight_mixture_amd", "csrc",
+                                                                   "gemm.hip"), "rb").read()).hexdigest()}
+    per_kernel = {}
+    for ctr, key in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
+        for kname, vals in _counter_rows(os.path.join(d, f"pmc_{ctr}")).items():
+            call = _gemm_call(kname)
+            if call is None:
+                continue
+            b = float(np.mean(vals)) * 1024 * scale[ctr]
+            rec[f"{call}_{key}_bytes"] = rec.get(f"{call}_{key}_bytes", 0.0) + b
+            short = re.search(r"gemm\w*<[^>]*>", kname).group(0)
+            per_kernel.setdefault(short, {})[key + "_bytes"] = b
+            per_kernel[short]["dispatches"] = len(vals)
+    for call in ("fc1", "fc2"):
+        rec[f"{call}_bytes"] = rec.get(f"{call}_read_bytes", 0.0) + rec.get(f"{call}_write_bytes", 0.0)
+    rec["scale"] = scale
+    rec["per_kernel"] = per_kernel
+    out = os.path.join(ROOT, "profiles", f"gemm_traffic_{name}" + (f"_t{shape.T}" if name == "decode" else "")
+                       + ".json")
+    json.dump(rec, open(out, "w"), indent=1)
+    print(json.dumps({k: v for k, v in rec.items() if k != "per_kernel"}))
+
+
+def measured_traffic(workload, inter, call, w_format, T=None):
     """HBM bytes (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration)
     of one `call` ("fc1"/"fc2"), as the rocprofv3 counter runs under profiles/
     recorded them, or None when there is no record for this workload or the
     grouped-GEMM source has changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}.json")
+    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}" + (f"_t{T}" if workload == "decode" else "")
+                        + ".json")
     if not os.path.exists(path):
         return None
     rec = json.load(open(path))
+    if T is not None and rec.get("T", T) != T:
+        return None
     src = os.path.join(ROOT, "mxfp4_weight_mixture_amd", "csrc", "gemm.hip")
     sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
     if rec.get("gemm_source_sha256") != sha or rec.get("intermediate_dtype") != inter \
@@ -551,6 +620,9 @@ def bench_streamed(args):
 
 def main():
     args = parse()
+    if args.traffic_record:
+        write_traffic_record(args)
+        return
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only (asked for --gpus {args.gpus}); the layer is not sharded "
               f"across GPUs in this build.", file=sys.stderr)

@@ -112,7 +112,9 @@ def _offsets(counts):
     return np.concatenate([[0], np.cumsum(counts)]).astype(np.int32)
 
 
-@pytest.mark.parametrize("K", [160, 512])   # 160: register-staged kernels; 512: three-stage DMA kernels
+# 160: register-staged kernels; 512 / 1024 / 1536 / 2560: three-stage DMA kernels with
+# one to five groups of four stages
+@pytest.mark.parametrize("K", [160, 512, 1024, 1536, 2560])
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("counts", [[40, 0, 300], [1, 33, 64, 65, 129, 256, 257]])
 def test_gemm_one_hot_rows_return_the_dequantised_weights_bitwise(fp8, counts, K):
@@ -196,6 +198,60 @@ def test_gemm_random_against_oracle(fp8, layout, K):
     # bf16 MFMA: fp32 accumulation (measured ~1e-6).  Scaled FP8 x FP4 MFMA:
     # its internal accumulation is slightly coarser (measured 1.5e-5 to 1.7e-5).
     assert rel_err(c.cpu().numpy(), want) < (1e-4 if fp8 else 1e-5)
+
+
+@pytest.mark.parametrize("K", [1024, 2048, 4096])
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("layout", ["none", "split"])
+def test_gemm_small_tiles_long_k_against_oracle(fp8, layout, K):
+    """Experts of at most 32 rows (the 32-row class, which streams weights) with
+    long K and gathered rows, against the oracle."""
+    g = np.random.default_rng(K + fp8)
+    counts = [1, 7, 32, 0, 19, 32, 3]
+    E, N = len(counts), 512
+    off = _offsets(counts)
+    rows = int(off[-1])
+    T, div = rows // 2 + 1, 2
+    perm_src = g.permutation(2 * T)[:rows].astype(np.int32)      # rows gathered from x[perm_src // 2]
+    x = torch.from_numpy(g.standard_normal((T, K)).astype(np.float32)).to(torch.bfloat16)
+    wp, ws = _rand_w(E, N, K, seed=K)
+    if fp8:
+        codes, scales = gen.quantize_mxfp8(x.float())
+        a, a_sc = codes.to(DEV), scales.to(DEV)
+        a64 = omx.dequant_mxfp8(codes.numpy(), scales.numpy())
+    else:
+        a, a_sc = x.to(DEV), None
+        a64 = omx.bf16_value(x.view(torch.int16).numpy())
+    c = mx.grouped_gemm(a, torch.from_numpy(wp).to(DEV), torch.from_numpy(ws).to(DEV),
+                        torch.from_numpy(off).to(DEV), a_scales=a_sc,
+                        a_gather=torch.from_numpy(perm_src).to(DEV), a_gather_div=div,
+                        epilogue=layout, out_dtype="fp32")
+    want = _gemm_oracle(a64, perm_src, div, wp, ws, off, layout)
+    assert rel_err(c.cpu().numpy(), want) < (1e-4 if fp8 else 1e-5)
+
+
+@pytest.mark.parametrize("K", [1024, 1536, 4096])
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("layout,out", [("none", "fp32"), ("none", "bf16"), ("split", "bf16")])
+def test_gemm_32_and_64_row_classes_agree_bitwise(fp8, layout, out, K):
+    """A 32-row expert (32-row tile class) and the first 32 rows of the same
+    expert given 33 rows (64-row class) accumulate every output in the same K
+    order, so they must agree bitwise."""
+    g = np.random.default_rng(3 * K + fp8)
+    N = 512
+    x = torch.from_numpy(g.standard_normal((33, K)).astype(np.float32)).to(torch.bfloat16)
+    wp, ws = _rand_w(1, N, K, seed=K + 1)
+    if fp8:
+        codes, scales = gen.quantize_mxfp8(x.float())
+        a, a_sc = codes.to(DEV), scales.to(DEV)
+    else:
+        a, a_sc = x.to(DEV), None
+    w = (torch.from_numpy(wp).to(DEV), torch.from_numpy(ws).to(DEV))
+    c32 = mx.grouped_gemm(a[:32], *w, torch.from_numpy(_offsets([32])).to(DEV),
+                          a_scales=a_sc[:32] if fp8 else None, epilogue=layout, out_dtype=out)
+    c33 = mx.grouped_gemm(a, *w, torch.from_numpy(_offsets([33])).to(DEV), a_scales=a_sc,
+                          epilogue=layout, out_dtype=out)
+    assert torch.equal(c32, c33[:32])
 
 
 @pytest.mark.parametrize("fp8", [False, True])
