@@ -43,9 +43,11 @@ __device__ inline uint32_t bf16_rne(float f) {
 // Rows are fetched kBatch at a time before any is accumulated (more loads in
 // flight per thread); the accumulation order stays j = 0, 1, ..., k-1.
 constexpr int kBatch = 8;
+constexpr int kThreads = 256;   // threads per token
+constexpr int kWaves = kThreads / 64;
 
 template <typename YT>
-__global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
+__global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict__ y,
                                                       const int32_t* __restrict__ dest_row,
                                                       const float* __restrict__ w, int k, int H,
                                                       float* __restrict__ out,
@@ -57,7 +59,7 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
   const int32_t* rows = dest_row + (size_t)t * k;
   const float* wt = w + (size_t)t * k;
   float ss = 0.f;
-  for (int v = threadIdx.x; v < nv; v += 256) {
+  for (int v = threadIdx.x; v < nv; v += kThreads) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < k; j0 += kBatch) {
       Raw raw[kBatch];
@@ -81,14 +83,17 @@ __global__ __launch_bounds__(256) void combine_kernel(const YT* __restrict__ y,
     for (int i = 0; i < 8; ++i) ss = fmaf(acc[i], acc[i], ss);
   }
   if (x_next == nullptr) return;  // uniform over the block
-  __shared__ float red[4];
+  __shared__ float red[kWaves];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
-  const float inv = 1.0f / sqrtf((red[0] + red[1] + red[2] + red[3]) / (float)H);
+  float tot = 0.f;
+#pragma unroll
+  for (int i = 0; i < kWaves; ++i) tot += red[i];
+  const float inv = 1.0f / sqrtf(tot / (float)H);
   uint16_t* xrow = x_next + (size_t)t * H;
-  for (int v = threadIdx.x; v < nv; v += 256) {
+  for (int v = threadIdx.x; v < nv; v += kThreads) {
     float o[8];
     load8(orow + 8 * v, o);  // this thread's own writes
     uint4 q;
@@ -106,10 +111,10 @@ moe_status launch_combine(const void* y, int y_dtype, const int32_t* dest_row, c
                           int T, int k, int H, float* out, uint16_t* x_next, hipStream_t s) {
   if (T == 0) return MOE_OK;
   if (y_dtype == MOE_OUT_BF16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(T), dim3(256), 0, s,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(T), dim3(kThreads), 0, s,
                        static_cast<const uint16_t*>(y), dest_row, w, k, H, out, x_next);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(256), 0, s,
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(kThreads), 0, s,
                        static_cast<const float*>(y), dest_row, w, k, H, out, x_next);
   MXMOE_HIP(hipGetLastError());
   return MOE_OK;
