@@ -112,3 +112,105 @@ def test_full_size_tiled_weights_equal_canonical_bitwise(name, over, inter):
     torch.cuda.synchronize()
     assert torch.equal(ref, got)
     print(f"[{name}] tiled == canonical bitwise", flush=True)
+
+
+def test_streamed_full_size_layers_routed_equals_all_and_oracle():
+    """The layerwise stream at its full shape (T=16384, hidden 4096, expert
+    intermediate 2048, 256 experts, top-6; pinned blobs of 3.42 GB, two HBM
+    slots, RMS chain), three layers over two distinct blobs: the routed expert
+    copy gives the all-experts stream's outputs and layer inputs bitwise (every
+    expert is hit at this T, so the copy kernel moves whole blobs), and sampled
+    tokens of every layer match the oracle on the recorded layer input."""
+    t0 = time.time()
+    s = gen.preset("streamed")
+    L, n_blobs = 3, 2
+    nbytes = mx.blob_bytes(s.H, s.I, s.E)
+    blobs = []
+    for b in range(n_blobs):
+        blob = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        for which, t in enumerate(gen.all_expert_weights(s, b, DEV)):
+            o = mx.blob_section_offset(s.H, s.I, s.E, which)
+            blob[o:o + t.numel()].copy_(t.reshape(-1))
+        blobs.append(blob)
+    torch.cuda.synchronize()
+    slots = [torch.empty(nbytes, dtype=torch.uint8, device=DEV) for _ in range(2)]
+    logits = torch.from_numpy(np.stack([gen.router_logits(s, l) for l in range(L)])).to(DEV)
+    x = gen.activations_bf16(s).to(DEV)
+    copy = torch.cuda.Stream()
+    res = {}
+    for mode in ("all", "routed"):
+        out = torch.empty((s.T, s.H), dtype=torch.float32, device=DEV)
+        caps = torch.empty((L, s.T, s.H), dtype=torch.bfloat16, device=DEV)
+        mx.prefill_streamed(blobs, slots, logits, x, out, T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, num_layers=L,
+                            layout=s.layout, chain="rms", depth=2, layer_inputs=caps, copy_stream=copy,
+                            expert_copy=mode)
+        torch.cuda.synchronize()
+        res[mode] = (out, caps)
+    assert torch.equal(res["all"][0], res["routed"][0]) and torch.equal(res["all"][1], res["routed"][1])
+    out, caps = res["all"]
+    assert torch.equal(caps[0], x) and torch.isfinite(out).all()
+    print(f"[streamed] gpu done {time.time() - t0:.1f}s", flush=True)
+    del slots, blobs
+    for l in range(L):
+        lg = logits[l].cpu().numpy()
+        rid, rw = omoe.route(lg, s.k)
+        toks = pick_tokens(rid, 3)
+        xin = omoe.activations(x_bf16=caps[l][torch.from_numpy(toks).to(DEV)].cpu().view(torch.int16).numpy())
+        ref = omoe.moe_tokens(xin, rid[toks], rw[toks], cpu_weights(s, l % n_blobs), s.layout)
+        if l + 1 < L:
+            got = caps[l + 1][torch.from_numpy(toks).to(DEV)].float().cpu().numpy()
+            want = omoe.rms_rescale(ref)
+        else:
+            got = out[torch.from_numpy(toks).to(DEV)].cpu().numpy()
+            want = ref
+        err = rel_err(got, want)
+        print(f"[streamed] layer {l} tokens {toks.tolist()} rel err {err:.3e} ({time.time() - t0:.1f}s)", flush=True)
+        assert err <= 2e-2
+
+
+def test_streamed_full_shape_small_batch_routed_copy_skips_unhit_experts():
+    """Full expert shapes (hidden 4096, intermediate 2048, 256 experts, top-6) at
+    T=32, where each layer hits only about half the experts: the routed stream
+    equals the all-experts stream bitwise, and in the last layer's slot every
+    expert the oracle's routing does not hit still holds the fill bytes."""
+    s = gen.preset("streamed", T=32)
+    L, fill = 2, 0xA5
+    nbytes = mx.blob_bytes(s.H, s.I, s.E)
+    blobs = []
+    for b in range(L):
+        blob = torch.empty(nbytes, dtype=torch.uint8, pin_memory=True)
+        for which, t in enumerate(gen.all_expert_weights(s, b, DEV)):
+            o = mx.blob_section_offset(s.H, s.I, s.E, which)
+            blob[o:o + t.numel()].copy_(t.reshape(-1))
+        blobs.append(blob)
+    torch.cuda.synchronize()
+    logits = torch.from_numpy(np.stack([gen.router_logits(s, l) for l in range(L)])).to(DEV)
+    x = gen.activations_bf16(s).to(DEV)
+    copy = torch.cuda.Stream()
+    res = {}
+    for mode in ("all", "routed"):
+        slots = [torch.full((nbytes,), fill, dtype=torch.uint8, device=DEV) for _ in range(2)]
+        out = torch.empty((s.T, s.H), dtype=torch.float32, device=DEV)
+        caps = torch.empty((L, s.T, s.H), dtype=torch.bfloat16, device=DEV)
+        mx.prefill_streamed(blobs, slots, logits, x, out, T=s.T, H=s.H, I=s.I, E=s.E, k=s.k, num_layers=L,
+                            layout=s.layout, chain="rms", depth=2, layer_inputs=caps, copy_stream=copy,
+                            expert_copy=mode)
+        torch.cuda.synchronize()
+        res[mode] = (out, caps, slots)
+    assert torch.equal(res["all"][0], res["routed"][0]) and torch.equal(res["all"][1], res["routed"][1])
+    slots = res["routed"][2]
+    per = [2 * s.I * (s.H // 2), 2 * s.I * (s.H // 32), s.H * (s.I // 2), s.H * (s.I // 32)]
+    for l in range(L):
+        hit = set(np.unique(omoe.route(logits[l].cpu().numpy(), s.k)[0]).tolist())
+        assert 0 < len(hit) < s.E
+        blob_dev = blobs[l].to(DEV)
+        for which in range(4):
+            o = mx.blob_section_offset(s.H, s.I, s.E, which)
+            sec = slots[l][o:o + s.E * per[which]].view(s.E, per[which])
+            ref = blob_dev[o:o + s.E * per[which]].view(s.E, per[which])
+            h = torch.tensor(sorted(hit), device=DEV)
+            u = torch.tensor(sorted(set(range(s.E)) - hit), device=DEV)
+            assert torch.equal(sec[h], ref[h])
+            assert bool((sec[u] == fill).all())
+        del blob_dev
+        print(f"[streamed T=32] layer {l}: {len(hit)} of {s.E} experts copied, the rest untouched", flush=True)
