@@ -1275,9 +1275,15 @@ moe_status launch_class(const Params& p, hipStream_t s, int reserve) {
 // the HBM-bound small-tile classes beside the full-tile class on a slice of
 // the CUs was measured slower: a few CUs cannot pull the weight stream at
 // HBM rate, and the full tiles lose those CUs for longer.)
+// Fewest rows an expert needs for a tile of each class (the planner's rule:
+// remainders of 1-32, 33-64, 65-128, 129-256 rows; full 128- or 256-row tiles
+// need at least that many).  A class whose minimum exceeds every expert's row
+// count gets no tiles and is not launched.
+constexpr int kClassMinRows[kClasses] = {1, 33, 65, 129};
+
 template <bool FP8, int EPI, int OUT, int PATH>
 moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* counts, hipStream_t s,
-                      int reserve) {
+                      int reserve, int max_rows) {
   int32_t* const ctr = p.unit_ctr;
   auto at = [&](int c) {
     p.tiles = lists + c * cap;
@@ -1285,8 +1291,11 @@ moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* count
     p.unit_ctr = ctr + c * kXcds;
   };
   at(0); MXMOE_TRY((launch_class<32, FP8, EPI, OUT, PATH>(p, s, reserve)));
+  if (max_rows < kClassMinRows[1]) return MOE_OK;
   at(1); MXMOE_TRY((launch_class<64, FP8, EPI, OUT, PATH>(p, s, reserve)));
+  if (max_rows < kClassMinRows[2]) return MOE_OK;
   at(2); MXMOE_TRY((launch_class<128, FP8, EPI, OUT, PATH>(p, s, reserve)));
+  if (max_rows < kClassMinRows[3]) return MOE_OK;
   // the bf16 DMA kernel's full tile is 128 rows (its 256-row stages do not fit
   // in LDS), so its class-3 list is empty
   if constexpr (!(PATH != 0 && !FP8)) {
@@ -1297,28 +1306,30 @@ moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* count
 
 template <bool FP8, int EPI, int PATH>
 moe_status dispatch_out(const Params& p, int c_dtype, const Tile* lists, int cap,
-                        const int32_t* counts, hipStream_t s, int reserve) {
-  if (c_dtype == MOE_OUT_FP32) return launch_all<FP8, EPI, MOE_OUT_FP32, PATH>(p, lists, cap, counts, s, reserve);
-  if (c_dtype == MOE_OUT_BF16) return launch_all<FP8, EPI, MOE_OUT_BF16, PATH>(p, lists, cap, counts, s, reserve);
+                        const int32_t* counts, hipStream_t s, int reserve, int max_rows) {
+  if (c_dtype == MOE_OUT_FP32)
+    return launch_all<FP8, EPI, MOE_OUT_FP32, PATH>(p, lists, cap, counts, s, reserve, max_rows);
+  if (c_dtype == MOE_OUT_BF16)
+    return launch_all<FP8, EPI, MOE_OUT_BF16, PATH>(p, lists, cap, counts, s, reserve, max_rows);
   if constexpr (PATH != 0 && EPI != 0)
-    return launch_all<FP8, EPI, MOE_OUT_MXFP8_E4M3, PATH>(p, lists, cap, counts, s, reserve);
+    return launch_all<FP8, EPI, MOE_OUT_MXFP8_E4M3, PATH>(p, lists, cap, counts, s, reserve, max_rows);
   return fail(MOE_ERR_NOT_IMPLEMENTED,
               "grouped GEMM: MXFP8 output needs the SwiGLU epilogue and K %% 512 == 0");
 }
 
 template <bool FP8, int PATH>
 moe_status dispatch_epi(const Params& p, int epi, int c_dtype, const Tile* lists, int cap,
-                        const int32_t* counts, hipStream_t s, int reserve) {
-  if (epi == MOE_EPI_NONE) return dispatch_out<FP8, 0, PATH>(p, c_dtype, lists, cap, counts, s, reserve);
-  return dispatch_out<FP8, 1, PATH>(p, c_dtype, lists, cap, counts, s, reserve);
+                        const int32_t* counts, hipStream_t s, int reserve, int max_rows) {
+  if (epi == MOE_EPI_NONE) return dispatch_out<FP8, 0, PATH>(p, c_dtype, lists, cap, counts, s, reserve, max_rows);
+  return dispatch_out<FP8, 1, PATH>(p, c_dtype, lists, cap, counts, s, reserve, max_rows);
 }
 
 template <bool FP8>
 moe_status dispatch_path(int path, const Params& p, int epi, int c_dtype, const Tile* lists, int cap,
-                         const int32_t* counts, hipStream_t s, int reserve) {
-  if (path == 2) return dispatch_epi<FP8, 2>(p, epi, c_dtype, lists, cap, counts, s, reserve);
-  if (path == 1) return dispatch_epi<FP8, 1>(p, epi, c_dtype, lists, cap, counts, s, reserve);
-  return dispatch_epi<FP8, 0>(p, epi, c_dtype, lists, cap, counts, s, reserve);
+                         const int32_t* counts, hipStream_t s, int reserve, int max_rows) {
+  if (path == 2) return dispatch_epi<FP8, 2>(p, epi, c_dtype, lists, cap, counts, s, reserve, max_rows);
+  if (path == 1) return dispatch_epi<FP8, 1>(p, epi, c_dtype, lists, cap, counts, s, reserve, max_rows);
+  return dispatch_epi<FP8, 0>(p, epi, c_dtype, lists, cap, counts, s, reserve, max_rows);
 }
 
 }  // namespace
@@ -1393,7 +1404,7 @@ moe_status launch_tile(const uint8_t* src_p, const uint8_t* src_s, int E, int N,
   return MOE_OK;
 }
 
-moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s, int reserve) {
+moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s, int reserve, int max_rows) {
   if (a.rows == 0) return MOE_OK;
   const int cap = list_capacity(a.rows, a.E);
   Tile* lists = static_cast<Tile*>(ws);
@@ -1431,8 +1442,10 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s, int rese
     p.n_tiles = (p.n_out + kBN / 2 - 1) / (kBN / 2);
   }
   const int path = !dma ? 0 : (a.w_format == MOE_W_TILED ? 2 : 1);
-  if (fp8) return dispatch_path<true>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s, reserve);
-  return dispatch_path<false>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s, reserve);
+  // no expert holds more rows than the call (or than the caller's bound)
+  const int mr = max_rows < 0 || max_rows > a.rows ? a.rows : max_rows;
+  if (fp8) return dispatch_path<true>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s, reserve, mr);
+  return dispatch_path<false>(path, p, a.epilogue, a.c_dtype, lists, cap, counts, s, reserve, mr);
 }
 
 }  // namespace mxmoe

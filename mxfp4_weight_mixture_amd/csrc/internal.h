@@ -41,8 +41,10 @@ size_t permute_ws_bytes(int T, int E, int k);
 moe_status launch_permute(const int32_t* ids, int T, int E, int k, int32_t* off, int32_t* perm_src,
                           int32_t* dest_row, void* ws, hipStream_t s);
 size_t gemm_ws_bytes(int rows, int E);
-// reserve: CUs per XCD that the persistent GEMM launches leave free (0: none)
-moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s, int reserve = 0);
+// reserve: CUs per XCD that the persistent GEMM launches leave free (0: none).
+// max_rows: a bound on any expert's row count (-1: the call's rows); row-tile
+// classes no expert can fill are not launched.
+moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s, int reserve = 0, int max_rows = -1);
 moe_status launch_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* w,
                           int T, int k, int H, float* out, uint16_t* x_next, hipStream_t s);
 moe_status validate_gemm(const moe_gemm_args& a);

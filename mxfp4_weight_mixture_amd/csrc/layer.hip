@@ -130,7 +130,9 @@ moe_status run_routing(const float* logits, int T, int E, int k, const Routing& 
 
 // FC1 + SwiGLU -> FC2 -> combine of a routed layer, all arguments valid, T > 0;
 // intermediate, FC2 output and GEMM scratch in a.workspace.  `reserve`: CUs
-// per XCD the GEMMs leave free.
+// per XCD the GEMMs leave free.  The routing picks k distinct experts per
+// token, so no expert has more than T rows: the GEMMs skip the row-tile
+// classes that need more (at T <= 32 only the 32-row class runs).
 moe_status run_experts(const moe_layer_args& a, const Routing& r, hipStream_t s, int reserve) {
   const LayerWs L = layer_ws_layout(a.T, a.H, a.I, a.E, a.k, a.inter_dtype);
   uint8_t* ws = static_cast<uint8_t*>(a.workspace);
@@ -155,7 +157,7 @@ moe_status run_experts(const moe_layer_args& a, const Routing& r, hipStream_t s,
   g1.c_scales = a.inter_dtype == MOE_OUT_MXFP8_E4M3 ? ws + L.inter_scales : nullptr;
   g1.c_dtype = a.inter_dtype;
   g1.w_format = a.w_format;
-  MXMOE_TRY(launch_gemm(g1, ws + L.gemm_ws, s, reserve));
+  MXMOE_TRY(launch_gemm(g1, ws + L.gemm_ws, s, reserve, a.T));
 
   moe_gemm_args g2{};
   g2.a = ws + L.inter;
@@ -175,7 +177,7 @@ moe_status run_experts(const moe_layer_args& a, const Routing& r, hipStream_t s,
   g2.c = ws + L.y;
   g2.c_dtype = MOE_OUT_BF16;
   g2.w_format = a.w_format;
-  MXMOE_TRY(launch_gemm(g2, ws + L.gemm_ws, s, reserve));
+  MXMOE_TRY(launch_gemm(g2, ws + L.gemm_ws, s, reserve, a.T));
 
   return launch_combine(ws + L.y, MOE_OUT_BF16, r.dest_row, r.w, a.T, a.k, a.H, a.out, a.x_next, s);
 }
