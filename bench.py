@@ -578,6 +578,10 @@ def bench_streamed(args):
     ms = float(np.mean(times))
     copy_ms = [ev[4 * l].elapsed_time(ev[4 * l + 1]) for l in range(L)]
     comp_ms = [ev[4 * l + 2].elapsed_time(ev[4 * l + 3]) for l in range(L)]
+    # overlap of the last timed pass: 1 - (time the compute stream sits idle) / wall, from the
+    # first copy's start to the last layer's end
+    span = ev[0].elapsed_time(ev[4 * (L - 1) + 3])
+    overlap = 1.0 - (span - sum(comp_ms)) / span
     # serialized comparison (depth 1: copy, compute, copy, ...)
     a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     a.record()
@@ -612,6 +616,8 @@ def bench_streamed(args):
         "h2d_GBps": achieved, "h2d_measured_peak_GBps": h2d_peak, "h2d_frac_of_measured": achieved / h2d_peak,
         "serialized_ms": ms1, "serialized_tokens_per_s": T / (ms1 * 1e-3),
         "per_layer_copy_ms_mean": float(np.mean(copy_ms)), "per_layer_compute_ms_mean": float(np.mean(comp_ms)),
+        "compute_busy_fraction": overlap,
+        "copy_busy_fraction": sum(copy_ms) / span,
         "roofline": {"bound": "h2d", "achieved": achieved, "peak": h2d_peak, "unit": "GB/s",
                      "frac": achieved / h2d_peak, "traffic": None, "kernel": "host->device weight stream"},
     }
