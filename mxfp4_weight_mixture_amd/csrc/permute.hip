@@ -75,27 +75,44 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   const int lane = threadIdx.x;
   const bool has_entries = n > 0;
   const int32_t* first = chunk_first + (size_t)blockIdx.x * E;
+  const int base = blockIdx.x * kChunk;
+  // this chunk's ids, all in flight while the offsets are scanned below
+  constexpr int kSteps = kChunk / 64;
+  int idv[kSteps];
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const int f = base + q * 64 + lane;
+    idv[q] = f < n ? ids[f] : 0;
+  }
+  // the totals go through LDS first (independent loads, several in flight), so
+  // that the scan below waits on LDS, not on a global load per 64 experts
+#pragma unroll 8
+  for (int e = lane; e < E; e += 64) pos[e] = totals[e];
+  __syncthreads();
   int carry = 0;
   for (int e0 = 0; e0 < E; e0 += 64) {
     const int e = e0 + lane;
-    const int v = e < E ? totals[e] : 0;
+    const int v = e < E ? pos[e] : 0;
     const int incl = wave_inclusive_scan(v, lane);
     if (e < E) {
       const int start = carry + incl - v;
-      if (has_entries) pos[e] = start + first[e];
+      pos[e] = start;
       if (blockIdx.x == 0) offsets[e] = start;
     }
     carry += __shfl(incl, 63, 64);
   }
   if (blockIdx.x == 0 && lane == 0) offsets[E] = carry;
   if (!has_entries) return;
+  // this chunk's first row of each expert
+#pragma unroll 8
+  for (int e = lane; e < E; e += 64) pos[e] += first[e];
   __syncthreads();
   const uint64_t below = (1ull << lane) - 1ull;
-  const int base = blockIdx.x * kChunk;
-  for (int s = 0; s < kChunk; s += 64) {
-    const int f = base + s + lane;
+#pragma unroll
+  for (int q = 0; q < kSteps; ++q) {
+    const int f = base + q * 64 + lane;
     const bool valid = f < n;
-    const int e = valid ? ids[f] : 0;
+    const int e = idv[q];
     uint64_t same = __ballot(valid);
     for (int b = 0; b < nbits; ++b) {
       const bool bit = (e >> b) & 1;

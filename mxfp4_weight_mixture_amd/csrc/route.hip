@@ -34,13 +34,31 @@ __device__ inline float key_value(uint32_t key) {
   return __uint_as_float((key & 0x80000000u) ? (key & 0x7fffffffu) : ~key);
 }
 
+// One step of the wave maximum: max(v, v of the lane the DPP control names);
+// lanes with no source compare against 0, below every key.
+template <int CTRL>
+__device__ inline uint64_t dpp_max_step(uint64_t v) {
+  const uint32_t lo = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)v, CTRL, 0xf, 0xf, false);
+  const uint32_t hi = __builtin_amdgcn_update_dpp(0, (int)(uint32_t)(v >> 32), CTRL, 0xf, 0xf, false);
+  const uint64_t o = ((uint64_t)hi << 32) | lo;
+  return o > v ? o : v;
+}
+
+// Largest key of the wave, in every lane.  Row shifts by 1, 2, 4 and 8 leave
+// each 16-lane row's maximum in its lane 15; the row-15 broadcast (to the next
+// row) and the row-31 broadcast (to rows 2 and 3) carry the wave's maximum to
+// lane 63, which readlane hands to every lane.  Register-to-register moves,
+// no LDS round trip per step.
 __device__ inline uint64_t wave_max_u64(uint64_t v) {
-#pragma unroll
-  for (int off = 32; off > 0; off >>= 1) {
-    uint64_t o = __shfl_xor(v, off, 64);
-    v = o > v ? o : v;
-  }
-  return v;
+  v = dpp_max_step<0x111>(v);   // row_shr:1
+  v = dpp_max_step<0x112>(v);   // row_shr:2
+  v = dpp_max_step<0x114>(v);   // row_shr:4
+  v = dpp_max_step<0x118>(v);   // row_shr:8
+  v = dpp_max_step<0x142>(v);   // row_bcast:15
+  v = dpp_max_step<0x143>(v);   // row_bcast:31
+  const uint32_t lo = __builtin_amdgcn_readlane((int)(uint32_t)v, 63);
+  const uint32_t hi = __builtin_amdgcn_readlane((int)(uint32_t)(v >> 32), 63);
+  return ((uint64_t)hi << 32) | lo;
 }
 
 __device__ inline double wave_sum_f64(double v) {
@@ -57,20 +75,31 @@ __global__ __launch_bounds__(256) void route_kernel(const float* __restrict__ lo
   if (t >= T) return;  // uniform per wave
   const float* row = logits + (size_t)t * E;
 
+  // all of a lane's logits in flight at once: an in-range (clamped) address
+  // under a wave-uniform guard, keys formed only after every load is issued
+  const int nv = (E + 63) / 64;
+  float val[kPerLane];
+#pragma unroll
+  for (int i = 0; i < kPerLane; ++i) val[i] = i < nv ? row[min(i * 64 + lane, E - 1)] : 0.f;
   uint64_t cand[kPerLane];
 #pragma unroll
   for (int i = 0; i < kPerLane; ++i) {
     const int e = i * 64 + lane;
-    cand[i] = (e < E) ? (((uint64_t)order_key(row[e]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e))
-                      : 0ull;
+    cand[i] = (e < E) ? (((uint64_t)order_key(val[i]) << 32) | (uint64_t)(0xffffffffu - (uint32_t)e)) : 0ull;
   }
 
   int my_id = 0;
   uint32_t my_key = 0u;
   for (int j = 0; j < k; ++j) {
-    uint64_t best = 0ull;
+    // lane-local maximum as a tree (depth 4 instead of a chain of 16)
+    uint64_t m[kPerLane];
 #pragma unroll
-    for (int i = 0; i < kPerLane; ++i) best = cand[i] > best ? cand[i] : best;
+    for (int i = 0; i < kPerLane; ++i) m[i] = cand[i];
+#pragma unroll
+    for (int w = kPerLane / 2; w > 0; w /= 2)
+#pragma unroll
+      for (int i = 0; i < w; ++i) m[i] = m[i + w] > m[i] ? m[i + w] : m[i];
+    const uint64_t best = m[0];
     const uint64_t win = wave_max_u64(best);
     // the id part is unique, so exactly one register of one lane holds `win`
 #pragma unroll
