@@ -131,6 +131,61 @@ __global__ __launch_bounds__(64) void scatter_kernel(const int32_t* __restrict__
   }
 }
 
+// All of a permutation that fits one chunk (n <= kChunk) in one block of 256
+// threads: LDS histogram, block scan of the counts (each thread a run of
+// consecutive experts), then the same stable scatter as scatter_kernel, by
+// wave 0.  One launch instead of three for decode-sized batches.
+__global__ __launch_bounds__(256) void permute_one_chunk_kernel(const int32_t* __restrict__ ids, int n, int E,
+                                                                int nbits, int32_t* __restrict__ offsets,
+                                                                int32_t* __restrict__ perm_src,
+                                                                int32_t* __restrict__ dest_row) {
+  extern __shared__ int pos[];
+  __shared__ int wave_sum[4];
+  const int tid = threadIdx.x, lane = tid & 63, wid = tid >> 6;
+  for (int e = tid; e < E; e += 256) pos[e] = 0;
+  __syncthreads();
+  for (int f = tid; f < n; f += 256) atomicAdd(&pos[ids[f]], 1);
+  __syncthreads();
+  // exclusive scan over the experts: thread tid owns experts [tid*R, tid*R + R)
+  const int R = (E + 255) / 256;
+  const int e0 = tid * R, e1 = min(E, e0 + R);
+  int run = 0;
+  for (int e = e0; e < e1; ++e) run += pos[e];
+  const int incl = wave_inclusive_scan(run, lane);
+  if (lane == 63) wave_sum[wid] = incl;
+  __syncthreads();
+  int start = incl - run;
+  for (int w = 0; w < wid; ++w) start += wave_sum[w];
+  for (int e = e0; e < e1; ++e) {
+    const int c = pos[e];
+    pos[e] = start;
+    offsets[e] = start;
+    start += c;
+  }
+  if (tid == 0) offsets[E] = n;
+  __syncthreads();
+  if (wid != 0) return;
+  const uint64_t below = (1ull << lane) - 1ull;
+  for (int s0 = 0; s0 < n; s0 += 64) {
+    const int f = s0 + lane;
+    const bool valid = f < n;
+    const int e = valid ? ids[f] : 0;
+    uint64_t same = __ballot(valid);
+    for (int b = 0; b < nbits; ++b) {
+      const bool bit = (e >> b) & 1;
+      const uint64_t m = __ballot(bit);
+      same &= bit ? m : ~m;
+    }
+    const int p0 = valid ? pos[e] : 0;
+    if (valid) {
+      const int row = p0 + __popcll(same & below);
+      perm_src[row] = f;
+      dest_row[f] = row;
+      if ((same & below) == 0) pos[e] = p0 + __popcll(same);
+    }
+  }
+}
+
 }  // namespace
 
 size_t permute_ws_bytes(int T, int E, int k) {
@@ -149,6 +204,12 @@ moe_status launch_permute(const int32_t* ids, int T, int E, int k, int32_t* off,
   const size_t lds = (size_t)E * sizeof(int);
   int nbits = 0;
   while ((1 << nbits) < E) ++nbits;
+  if (nchunks == 1) {
+    hipLaunchKernelGGL(permute_one_chunk_kernel, dim3(1), dim3(256), lds, s, ids, n, E, nbits, off, perm_src,
+                       dest_row);
+    MXMOE_HIP(hipGetLastError());
+    return MOE_OK;
+  }
   if (nchunks > 0) {
     hipLaunchKernelGGL(hist_kernel, dim3(nchunks), dim3(256), lds, s, ids, n, E, counts);
     MXMOE_HIP(hipGetLastError());

@@ -71,7 +71,9 @@ def _perm_check(ids_np, E):
     np.testing.assert_array_equal(dr.cpu().numpy(), rdr)
 
 
-@pytest.mark.parametrize("T,E,k", [(32, 4, 2), (257, 896, 16), (1, 5, 1), (4096, 256, 6), (3, 1, 1)])
+# T*k <= 1024 runs the one-block permutation; (64, 896, 16) is exactly one chunk, (1025, 7, 1) one entry more
+@pytest.mark.parametrize("T,E,k", [(32, 4, 2), (257, 896, 16), (1, 5, 1), (4096, 256, 6), (3, 1, 1),
+                                   (64, 896, 16), (1025, 7, 1), (100, 8192, 8), (1, 896, 16)])
 def test_permute_bit_exact(T, E, k):
     g = np.random.default_rng(T + E + k)
     lg = g.standard_normal((T, E)).astype(np.float32)
