@@ -1,6 +1,7 @@
-"""Full-size workloads, in the launch configuration the benchmark times: routing
-and permutation bit-exact over every token, and the layer output on sampled
-tokens against the oracle (which regenerates only the experts those tokens use)."""
+"""Full-size workloads, in the launch configuration the benchmark times (weights
+tiled at load): routing and permutation bit-exact over every token, and the
+layer output on sampled tokens against the oracle (which regenerates only the
+experts those tokens use)."""
 import time
 
 import numpy as np
@@ -34,13 +35,15 @@ def _full(name, n_sample, tol, inter="bf16", **over):
     s = gen.preset(name, **over)
     li = gen.layer_inputs(s)
     w = device_weights(s)
-    layer = mx.Layer(*w, k=s.k, layout=s.layout, inter=inter)
+    # the benchmark's configuration: weights tiled once at load (one resident copy)
+    layer = mx.Layer(*w, k=s.k, layout=s.layout, inter=inter, tile=True)
+    del w
     x, xs = device_x(li)
     out = layer.forward(torch.from_numpy(li.logits).to(DEV), x, xs)
     torch.cuda.synchronize()
     r = {k: v.cpu().numpy() for k, v in layer.routing(s.T).items()}
     out = out.cpu().numpy()
-    del w, layer, x, xs
+    del layer, x, xs
     torch.cuda.empty_cache()
     print(f"[{name} inter={inter}] gpu done {time.time() - t0:.1f}s", flush=True)
 
@@ -74,8 +77,9 @@ def test_prefill256_full_size():
     _full("prefill256", 6, 2e-2)
 
 
-def test_decode_t1_full_size():
-    _full("decode", 1, 2e-2, T=1)
+@pytest.mark.parametrize("T,n", [(1, 1), (2, 1), (8, 2), (32, 2)])
+def test_decode_full_size(T, n):
+    _full("decode", n, 2e-2, T=T)
 
 
 def test_prefill896_repeat_runs_bitwise_identical():
