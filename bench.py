@@ -67,6 +67,8 @@ def parse():
                         "and intermediate are multiples of 512, else canonical)")
     p.add_argument("--expert-copy", default="all", choices=["all", "routed", "auto"],
                    help="streamed: move every expert per layer, or only the experts the layer's routing hits")
+    p.add_argument("--mfma-rate", action="store_true",
+                   help="issue rates of the matrix instructions the GEMM uses (libmxmoe_probe.so), one JSON line")
     p.add_argument("--traffic-record", default=None, metavar="DIR",
                    help="write profiles/gemm_traffic_<workload>.json from the rocprofv3 counter runs under DIR "
                         "(subfolders pmc_FETCH_SIZE, pmc_WRITE_SIZE, cal_FETCH_SIZE, cal_WRITE_SIZE); no GPU needed")
@@ -624,6 +626,37 @@ def bench_streamed(args):
     return rec
 
 
+def mfma_rates():
+    """Sustained rate of each matrix instruction the grouped GEMM issues, over the whole chip (two blocks of
+    four waves per CU, eight independent accumulators per wave), with constant operands and with operand bits
+    that change every round.  The ceilings FC1 / FC2 are read against."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_weight_mixture_amd", "libmxmoe_probe.so"))
+    fn = lib.mxmoe_probe_mfma_rate
+    fn.restype = ctypes.c_float
+    fn.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    blocks = 2 * cus
+    out = torch.empty(blocks * 256, dtype=torch.float32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rec = {"probe": "mfma issue rate", "cus": cus, "blocks": blocks, "waves_per_cu": 8,
+           "command": "python bench.py --mfma-rate"}
+    for kind, name, fl in ((0, "fp8xfp4_scaled_32x32x64", 2 * 32 * 32 * 64), (1, "fp4xfp4_scaled_32x32x64", 2 * 32 * 32 * 64),
+                           (2, "bf16_32x32x16", 2 * 32 * 32 * 16)):
+        for vary in (0, 1):
+            fn(kind, blocks, 2000, vary, out.data_ptr(), stream)          # warm-up (clocks, code load)
+            iters = 100000 if kind != 2 else 200000
+            ms = fn(kind, blocks, iters, vary, out.data_ptr(), stream)
+            if ms <= 0:
+                raise RuntimeError("probe launch failed")
+            flops = 8.0 * iters * blocks * 4 * fl
+            rec[f"{name}_{'random' if vary else 'constant'}_PFLOPs"] = flops / (ms * 1e-3) / 1e15
+            log(f"[probe] {name} {'changing' if vary else 'constant'} operands: {flops / (ms * 1e-3) / 1e15:.2f} PF "
+                f"({ms:.1f} ms)")
+    return rec
+
+
 def main():
     args = parse()
     if args.traffic_record:
@@ -637,6 +670,9 @@ def main():
         print("bench.py needs an MI355X (gfx950) GPU", file=sys.stderr)
         sys.exit(1)
 
+    if args.mfma_rate:
+        print(json.dumps(mfma_rates()))
+        return
     if args.copy_calibration:
         n = 1 << 30
         src = torch.ones(n // 4, dtype=torch.float32, device="cuda")
