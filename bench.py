@@ -540,8 +540,9 @@ def bench_streamed(args):
     out = torch.empty((T, H), dtype=torch.float32, device=dev)
     copy = torch.cuda.Stream()
     ws = None
-    # measured pinned H2D peak on the same buffers (copy engine, one stream)
-    h2d = []
+    # measured pinned H2D peak on the same buffers (copy engine): whole blobs on one stream, and
+    # 16 MB .. 1 GB pieces on one and on two streams; the best is the denominator
+    h2d = {}
     for b in range(min(2, n_blobs)):
         e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         with torch.cuda.stream(copy):
@@ -549,8 +550,30 @@ def bench_streamed(args):
             slots[b % 2].copy_(blobs[b], non_blocking=True)
             e1.record()
         copy.synchronize()
-        h2d.append(nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9)
-    h2d_peak = max(h2d)
+        h2d[f"blob_1stream_{b}"] = nbytes / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    copy2 = torch.cuda.Stream()
+    for size in (16 << 20, 256 << 20, 1 << 30):
+        reps = max(1, (2 << 30) // size)
+        for nstreams in (1, 2):
+            streams = [copy, copy2][:nstreams]
+            torch.cuda.synchronize()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record()
+            for st in streams:
+                st.wait_event(e0)
+            for r in range(reps):
+                st = streams[r % nstreams]
+                off = (r * size) % (nbytes - size)
+                with torch.cuda.stream(st):
+                    slots[r % 2][off:off + size].copy_(blobs[r % n_blobs][off:off + size], non_blocking=True)
+            cur = torch.cuda.current_stream()
+            for st in streams:
+                cur.wait_stream(st)
+            e1.record()
+            torch.cuda.synchronize()
+            h2d[f"{size >> 20}MB_{nstreams}stream"] = reps * size / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    h2d_peak = max(h2d.values())
+    log("[bench] pinned H2D GB/s: " + ", ".join(f"{k} {v:.1f}" for k, v in h2d.items()))
 
     def run(depth, events=None, expert_copy=args.expert_copy):
         nonlocal ws
@@ -616,6 +639,7 @@ def bench_streamed(args):
         "all_experts_ms": all_ms,
         "tflops": flops / (ms * 1e-3) / 1e12,
         "h2d_GBps": achieved, "h2d_measured_peak_GBps": h2d_peak, "h2d_frac_of_measured": achieved / h2d_peak,
+        "h2d_sweep_GBps": h2d,
         "serialized_ms": ms1, "serialized_tokens_per_s": T / (ms1 * 1e-3),
         "per_layer_copy_ms_mean": float(np.mean(copy_ms)), "per_layer_compute_ms_mean": float(np.mean(comp_ms)),
         "compute_busy_fraction": overlap,
