@@ -367,7 +367,9 @@ size_t     moe_streamed_workspace_size(int32_t T, int32_t H, int32_t I, int32_t 
  * copy and runs the layer.  The copy stream first waits for the compute
  * stream's earlier work.  Nothing waits on the host; on return both
  * streams hold the whole pass and `out` is ordered on `compute`.
- * MOE_ERR_NOT_PINNED if a blob is not page-locked host memory.
+ * MOE_ERR_NOT_PINNED if a blob is not page-locked host memory.  At depth 2
+ * the two streams must differ (MOE_ERR_INVALID_ARG otherwise: on one
+ * stream every copy would wait for the previous layer's compute).
  *
  * Routed expert copy (MOE_COPY_ROUTED, or MOE_COPY_AUTO with
  * T <= routed_copy_max_tokens): the router logits of every layer are inputs

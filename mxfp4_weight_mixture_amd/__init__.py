@@ -134,6 +134,30 @@ def _u8(n: int, device) -> torch.Tensor:
     return torch.empty(max(int(n), 1), dtype=torch.uint8, device=device)
 
 
+def _keep_until_done(stream, *tensors):
+    """Tensors allocated here on the current stream but used by work enqueued on
+    `stream`: tell the caching allocator so, so that it does not hand their memory
+    to a later allocation before that work has finished."""
+    if stream is None or stream == torch.cuda.current_stream(stream.device):
+        return
+    for t in tensors:
+        if t is not None:
+            t.record_stream(stream)
+
+
+_COPY_STREAMS = {}
+
+
+def _copy_stream_for(device) -> "torch.cuda.Stream":
+    """One side stream per device for the streamed prefill's copies when the caller gives none."""
+    idx = torch.device(device).index
+    if idx is None:
+        idx = torch.cuda.current_device()
+    if idx not in _COPY_STREAMS:
+        _COPY_STREAMS[idx] = torch.cuda.Stream(device=idx)
+    return _COPY_STREAMS[idx]
+
+
 def device_supported() -> bool:
     return lib.moe_device_supported() == 1
 
@@ -146,6 +170,7 @@ def route(logits: torch.Tensor, k: int, stream=None):
     ids = torch.empty((T, k), dtype=torch.int32, device=logits.device)
     w = torch.empty((T, k), dtype=torch.float32, device=logits.device)
     _check(lib.moe_route(_ptr(logits), T, E, k, _ptr(ids), _ptr(w), _stream(stream)))
+    _keep_until_done(stream, ids, w)
     return ids, w
 
 
@@ -160,6 +185,7 @@ def permute(topk_ids: torch.Tensor, E: int, stream=None):
     ws = _u8(n, dev)
     _check(lib.moe_permute(_ptr(topk_ids), T, E, k, _ptr(off), _ptr(ps), _ptr(dr), _ptr(ws), n,
                            _stream(stream)))
+    _keep_until_done(stream, off, ps, dr, ws)
     return off, ps, dr
 
 
@@ -198,6 +224,7 @@ def grouped_gemm(a: torch.Tensor, w_packed: torch.Tensor, w_scales: torch.Tensor
     n = lib.moe_grouped_gemm_workspace_size(ctypes.byref(args))
     ws = _u8(n, a.device)
     _check(lib.moe_mxfp4_grouped_gemm(ctypes.byref(args), _ptr(ws), n, _stream(stream)))
+    _keep_until_done(stream, c, c_scales, ws)
     return (c, c_scales) if c_dt == 2 else c
 
 
@@ -211,6 +238,7 @@ def tile_weights(w_packed: torch.Tensor, w_scales: torch.Tensor, epilogue: str =
     _check(lib.moe_mxfp4_tile_weights(_ptr(w_packed), _ptr(w_scales), E, N, 2 * K2,
                                       {"none": 0, "split": 1, "interleaved": 2}[epilogue], _ptr(tp), _ptr(ts),
                                       _stream(stream)))
+    _keep_until_done(stream, tp, ts)
     return tp, ts
 
 
@@ -221,6 +249,7 @@ def untile_weights(t_packed: torch.Tensor, t_scales: torch.Tensor, epilogue: str
     _check(lib.moe_mxfp4_untile_weights(_ptr(t_packed), _ptr(t_scales), E, N, 2 * K2,
                                         {"none": 0, "split": 1, "interleaved": 2}[epilogue], _ptr(wp), _ptr(ws),
                                         _stream(stream)))
+    _keep_until_done(stream, wp, ws)
     return wp, ws
 
 
@@ -234,6 +263,7 @@ def combine(y: torch.Tensor, dest_row: torch.Tensor, topk_w: torch.Tensor, *, rm
     dt = 1 if y.dtype == torch.bfloat16 else 0
     _check(lib.moe_combine(_ptr(y), dt, _ptr(dest_row), _ptr(topk_w), T, k, H, _ptr(out), _ptr(xn),
                            _stream(stream)))
+    _keep_until_done(stream, out, xn)
     return (out, xn) if rms_next else out
 
 
@@ -284,6 +314,8 @@ class Layer:
             out = torch.empty((T, self.H), dtype=torch.float32, device=logits.device)
         args = self._args(T, logits, x, x_scales, out, x_next, self._ws)
         _check(lib.moe_layer_forward(ctypes.byref(args), _stream(stream)))
+        # the workspace may be replaced by a larger one on a later call while this one still runs
+        _keep_until_done(stream, self._ws, out)
         return out
 
     def capture(self, logits: torch.Tensor, x: torch.Tensor, x_scales: Optional[torch.Tensor] = None,
@@ -374,6 +406,9 @@ def prefill_streamed(host_blobs: Sequence[torch.Tensor], slots: Sequence[torch.T
 
     expert_copy: "all" moves every expert of a layer, "routed" only the experts
     its routing hits, "auto" routed when T <= routed_copy_max_tokens.
+    copy_stream: the stream the weight copies run on; None uses one dedicated
+    side stream per device (never the compute stream, which would serialise the
+    pipeline).
     """
     nb = len(host_blobs)
     arr = (_vp * nb)(*[b.data_ptr() for b in host_blobs])
@@ -395,6 +430,11 @@ def prefill_streamed(host_blobs: Sequence[torch.Tensor], slots: Sequence[torch.T
                         w_format=W_FORMAT[w_format], expert_copy=EXPERT_COPY[expert_copy],
                         routed_copy_max_tokens=routed_copy_max_tokens)
     cs = _stream(compute_stream)
-    xs = _stream(copy_stream) if copy_stream is not None else cs
-    _check(lib.moe_layer_prefill_streamed(ctypes.byref(args), cs, xs))
+    if copy_stream is None:
+        # a copy on the compute stream would serialise the pipeline
+        copy_stream = _copy_stream_for(x.device)
+    _check(lib.moe_layer_prefill_streamed(ctypes.byref(args), cs, _stream(copy_stream)))
+    _keep_until_done(compute_stream, workspace)
+    if copy_stream != torch.cuda.current_stream(x.device):
+        workspace.record_stream(copy_stream)
     return workspace

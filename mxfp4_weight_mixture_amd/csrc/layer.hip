@@ -350,6 +350,11 @@ moe_status moe_layer_prefill_streamed(const moe_streamed_args* a, void* compute_
   for (int i = 0; i < a->depth; ++i)
     if (routed && reinterpret_cast<uintptr_t>(a->device_slot[i]) % 16)
       return fail(MOE_ERR_INVALID_ARG, "streamed: routed copy needs 16-byte aligned slots (slot %d)", i);
+  // one stream for both would run every copy after the previous layer's compute
+  if (a->depth == 2 && compute_stream == copy_stream)
+    return fail(MOE_ERR_INVALID_ARG,
+                "streamed: depth 2 needs a copy stream distinct from the compute stream (one stream serialises "
+                "the pipeline)");
   MXMOE_TRY(check_device());
   // the routed copy kernel reads each blob through the address the device
   // maps it at

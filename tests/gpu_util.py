@@ -38,3 +38,52 @@ def device_x(li, device="cuda"):
     if li.x_codes is not None:
         return li.x_codes.to(device), li.x_scales.to(device)
     return li.x_bf16.to(device), None
+
+
+# ------------------------------------------------- whole-output oracle runs
+
+_FULL = {}
+
+
+def full_oracle(shape, li, w_dev=None, label=""):
+    """The oracle's layer over every token of a workload, computed once per
+    workload shape in a test session and shared by the modules that need it.
+
+    w_dev: the canonical MXFP4 weights as the workload generator made them on
+    the device (the GPU path reads a tiled copy); each hit expert's bytes are
+    copied to the host when the oracle asks for that expert, which is cheaper
+    than regenerating them on the CPU.  Returns (out float64 [T][H], routing
+    dict of ids / w / offsets / perm_src / dest_row).
+    """
+    if shape in _FULL:
+        return _FULL[shape]
+    import time
+    t0 = time.time()
+    done = [0]
+    if w_dev is None:
+        base = cpu_weights(shape)
+    else:
+        def base(e):
+            return [t[e].cpu().numpy() for t in w_dev]
+
+    def fetch(e):
+        done[0] += 1
+        if done[0] % 64 == 0:
+            print(f"[oracle {label}] {done[0]} experts ({time.time() - t0:.0f}s)", flush=True)
+        return base(e)
+
+    out, it = omoe.moe_layer(x_as_f64(li), li.logits, shape.k, fetch, shape.layout, return_intermediates=True)
+    it.pop("Y")
+    print(f"[oracle {label}] whole layer: {done[0]} experts, {time.time() - t0:.1f}s", flush=True)
+    _FULL[shape] = (out, it)
+    return out, it
+
+
+def generator_matches_on_cpu(shape, w_dev, experts):
+    """The device-generated weights of the given experts equal the CPU generator's bytes."""
+    for e in experts:
+        cpu = gen.expert_weights(shape, int(e), 0, "cpu")
+        for d, c in zip(w_dev, cpu):
+            if not torch.equal(d[int(e)].cpu(), c):
+                return False
+    return True

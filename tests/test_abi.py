@@ -133,6 +133,18 @@ def test_routed_copy_rejects_misaligned_blobs_before_any_device_call():
     assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "16-byte aligned blobs" in msg
 
 
+def test_streamed_depth_2_needs_two_streams_before_any_device_call():
+    blob = (ctypes.c_uint8 * 4096)()
+    ptrs = (ctypes.c_void_p * 1)(ctypes.addressof(blob))
+    slots = (ctypes.c_void_p * 2)(256, 512)
+    args = mx.StreamedArgs(num_layers=2, T=4, H=128, I=64, E=4, k=2, layout=1, chain=0, depth=2, num_blobs=1,
+                           host_blobs=ptrs, blob_bytes=1 << 20, device_slot=slots, logits=256, x=256, out=256,
+                           workspace=256, workspace_bytes=1 << 30)
+    for cs in (None, 4096):
+        st, msg = _status(mx.lib.moe_layer_prefill_streamed(ctypes.byref(args), cs, cs))
+        assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "distinct" in msg
+
+
 def test_blob_layout_sections_are_aligned_and_ordered():
     H, I, E = 4096, 2048, 256
     offs = [mx.blob_section_offset(H, I, E, w) for w in range(4)]
