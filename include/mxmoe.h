@@ -205,6 +205,24 @@ size_t     moe_grouped_gemm_workspace_size(const moe_gemm_args* args);
 moe_status moe_mxfp4_grouped_gemm(const moe_gemm_args* args, void* workspace,
                                   size_t workspace_bytes, void* stream);
 
+/* For callers that cannot allocate device memory (code under HIP graph
+ * capture, tight serving loops, harnesses that forbid hipMalloc): the same
+ * grouped GEMM, with the same arguments, kernels and results as
+ * moe_mxfp4_grouped_gemm, but its scratch (the planner's tile lists, tile
+ * counts and unit counters) lives in a device array inside the library of
+ * MXMOE_STATIC_SCRATCH_BYTES bytes, which each device the library runs on
+ * holds until the process ends.  The call allocates and frees nothing.
+ * Limit: moe_grouped_gemm_workspace_size(args) <= MXMOE_STATIC_SCRATCH_BYTES
+ * (about rows / 32 + E <= 32 700; e.g. rows up to ~1 000 000 at E = 896),
+ * MOE_ERR_WORKSPACE above it (nothing enqueued).  Every call on a device
+ * shares that device's array: calls that overlap on one device (on different
+ * streams, or from different threads) race and must not be issued; calls
+ * ordered on one stream are safe.  The array keeps the last call's contents;
+ * the planner rewrites every word the GEMM reads, so nothing needs clearing.
+ * Errors as for moe_mxfp4_grouped_gemm. */
+#define MXMOE_STATIC_SCRATCH_BYTES (1u << 20)
+moe_status moe_mxfp4_grouped_gemm_static(const moe_gemm_args* args, void* stream);
+
 /* ----------------------------------------------- load-time weight tiling -- */
 
 /* Load-time repacking of one weight matrix into the order the grouped GEMM

@@ -82,6 +82,7 @@ def _load():
         "moe_permute": (ctypes.c_int, [_vp, _i32, _i32, _i32, _vp, _vp, _vp, _vp, _sz, _vp]),
         "moe_grouped_gemm_workspace_size": (_sz, [ctypes.POINTER(GemmArgs)]),
         "moe_mxfp4_grouped_gemm": (ctypes.c_int, [ctypes.POINTER(GemmArgs), _vp, _sz, _vp]),
+        "moe_mxfp4_grouped_gemm_static": (ctypes.c_int, [ctypes.POINTER(GemmArgs), _vp]),
         "moe_combine": (ctypes.c_int, [_vp, _i32, _vp, _vp, _i32, _i32, _i32, _vp, _vp, _vp]),
         "moe_layer_workspace_size": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32]),
         "moe_layer_workspace_offset": (_sz, [_i32, _i32, _i32, _i32, _i32, _i32, _i32]),

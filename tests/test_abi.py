@@ -145,6 +145,21 @@ def test_streamed_depth_2_needs_two_streams_before_any_device_call():
         assert st == mx.STATUS["MOE_ERR_INVALID_ARG"] and "distinct" in msg
 
 
+def test_static_scratch_gemm_checks_before_any_device_call():
+    st, msg = _status(mx.lib.moe_mxfp4_grouped_gemm_static(None, None))
+    assert st == mx.STATUS["MOE_ERR_INVALID_ARG"]
+    # 1.1 M rows over 896 experts need more planner scratch than the static array holds
+    args = mx.GemmArgs(a=256, w_packed=256, w_scales=256, expert_offsets=256, c=256, a_dtype=0, a_gather_div=1,
+                       a_rows=1_100_000, rows=1_100_000, E=896, N=7168, K=3584, epilogue=0, c_dtype=1, w_format=0)
+    assert mx.lib.moe_grouped_gemm_workspace_size(ctypes.byref(args)) > (1 << 20)
+    st, msg = _status(mx.lib.moe_mxfp4_grouped_gemm_static(ctypes.byref(args), None))
+    assert st == mx.STATUS["MOE_ERR_WORKSPACE"] and "static" in msg
+    # bad arguments are the same errors as the workspace entry point's
+    args.K = 100
+    st, msg = _status(mx.lib.moe_mxfp4_grouped_gemm_static(ctypes.byref(args), None))
+    assert st == mx.STATUS["MOE_ERR_SHAPE"]
+
+
 def test_blob_layout_sections_are_aligned_and_ordered():
     H, I, E = 4096, 2048, 256
     offs = [mx.blob_section_offset(H, I, E, w) for w in range(4)]
