@@ -187,76 +187,162 @@ def sanity_gate(shape, steps):
     return checks
 
 
-def cpu_baseline(shape, li, ids, budget_s=25.0):
-    """The oracle timed on this host on a bounded, stratified sample of the workload.
-
-    Its cost is per expert (dequantise, two matmuls over the expert's rows) plus
-    route/permute/combine.  Route and permute run in full; a stratified sample of
-    the hit experts (evenly spaced ranks by row count, largest included) runs
-    through the oracle's expert body with its real rows; a + b*rows is fitted
-    and summed over every hit expert; the combine is timed on a token subset
-    and scaled.  Reported as tokens/s for the whole layer.
-    """
-    from oracle import moe as omoe
-    from oracle import mx as omx
+def host_info():
+    """The host the CPU baseline ran on: CPU model, cores, NUMA nodes, BLAS library and its threads."""
+    import glob
+    info = {"cpu_count": os.cpu_count(), "affinity_cpus": len(os.sched_getaffinity(0))}
+    try:
+        with open("/proc/cpuinfo") as f:
+            info["cpu_model"] = next((l.split(":", 1)[1].strip() for l in f if l.startswith("model name")), None)
+    except OSError:
+        info["cpu_model"] = None
+    info["numa_nodes"] = len(glob.glob("/sys/devices/system/node/node[0-9]*")) or None
     try:
         from threadpoolctl import threadpool_info
-        threads = max([i.get("num_threads", 1) for i in threadpool_info()] + [1])
+        info["blas"] = [{k: i.get(k) for k in ("internal_api", "version", "num_threads", "threading_layer",
+                                                "architecture")} for i in threadpool_info() if i.get("user_api") == "blas"]
     except Exception:
-        threads = 1
+        info["blas"] = None
+    return info
+
+
+def _blas_threads(host):
+    return max([b.get("num_threads") or 1 for b in (host.get("blas") or [])] + [1])
+
+
+def _time_experts(shape, li, layer, budget_s):
+    """The oracle's expert body (dequantise both matrices + the SwiGLU MLP, float64) over this layer's
+    hit experts: every hit expert when the largest one's time x their count fits the budget (measured),
+    else a stratified sample by row count with t = a + b*rows fitted and summed (extrapolated).
+    Weights are generated before each timed expert (input generation, not timed)."""
+    from oracle import moe as omoe
+    from oracle import mx as omx
     t0 = time.perf_counter()
     rid, rw = omoe.route(li.logits, shape.k)
     offsets, perm_src, dest_row = omoe.permute(rid, shape.E)
     t_rp = time.perf_counter() - t0
     counts = np.diff(offsets)
     hit = np.nonzero(counts)[0]
-    order = hit[np.argsort(counts[hit], kind="stable")]
+    order = hit[np.argsort(-counts[hit], kind="stable")]          # largest first
+    x_rows = None
     if shape.act == "mxfp8":
-        xs_all = None
-    xb = li.x_bf16
-    samples = []
-    spent = 0.0
-    n_target = min(8, len(order))
-    picks = [order[int(round(q))] for q in np.linspace(0, len(order) - 1, n_target)]
-    for e in picks[::-1]:                       # largest first
-        if spent > budget_s and len(samples) >= 2:
-            break
+        x_rows = lambda tok: omoe.activations(x_codes=li.x_codes[tok].numpy(), x_scales=li.x_scales[tok].numpy())
+    else:
+        x_rows = lambda tok: omoe.activations(x_bf16=li.x_bf16[tok].view(torch.int16).numpy())
+
+    def one(e):
         lo, hi = int(offsets[e]), int(offsets[e + 1])
-        tok = perm_src[lo:hi] // shape.k
-        if shape.act == "mxfp8":
-            c, s_ = gen.quantize_mxfp8(xb[tok].float())
-            X = omoe.activations(x_codes=c.numpy(), x_scales=s_.numpy())
-        else:
-            X = omoe.activations(x_bf16=xb[tok].view(torch.int16).numpy())
-        w1p, w1s, w2p, w2s = [t.numpy() for t in gen.expert_weights(shape, int(e))]
+        X = x_rows(perm_src[lo:hi] // shape.k)
+        w1p, w1s, w2p, w2s = [t.numpy() for t in gen.expert_weights(shape, int(e), layer)]
         t1 = time.perf_counter()
         omoe.expert_mlp(X, omx.dequant_mxfp4(w1p, w1s), omx.dequant_mxfp4(w2p, w2s), shape.layout)
-        dt = time.perf_counter() - t1
-        spent += dt
-        samples.append((hi - lo, dt))
-    n = np.array([s[0] for s in samples], dtype=np.float64)
-    t = np.array([s[1] for s in samples], dtype=np.float64)
-    if len(samples) >= 2 and np.ptp(n) > 0:
-        b, a = np.polyfit(n, t, 1)
-        a = max(a, 0.0)
-        b = max(b, 0.0)
+        return hi - lo, time.perf_counter() - t1
+
+    first = one(order[0])
+    samples = [first]
+    if first[1] * len(order) <= budget_s:
+        samples += [one(e) for e in order[1:]]
+        t_exp, how = float(sum(t for _, t in samples)), f"all {len(hit)} hit experts timed"
     else:
-        a, b = float(t.mean()), 0.0
-    t_experts = float(len(hit) * a + b * counts[hit].sum())
-    # combine on a token subset, scaled
-    sub = min(shape.T, 256)
+        n_target = min(8, len(order))
+        picks = [order[int(round(q))] for q in np.linspace(0, len(order) - 1, n_target)][1:]
+        spent = first[1]
+        for e in picks:
+            if spent > budget_s and len(samples) >= 2:
+                break
+            samples.append(one(e))
+            spent += samples[-1][1]
+        n = np.array([s[0] for s in samples], dtype=np.float64)
+        t = np.array([s[1] for s in samples], dtype=np.float64)
+        if len(samples) >= 2 and np.ptp(n) > 0:
+            b, a = np.polyfit(n, t, 1)
+            a, b = max(a, 0.0), max(b, 0.0)
+        else:
+            a, b = float(t.mean()), 0.0
+        t_exp = float(len(hit) * a + b * counts[hit].sum())
+        how = (f"{len(samples)} of {len(hit)} hit experts timed at evenly spaced row-count ranks "
+               f"({', '.join(str(int(v)) for v in n)} rows), t = a + b*rows fitted (a={a:.3f}s, "
+               f"b={b * 1e3:.3f}ms/row) and summed over all hit experts")
+    # the combine, on all tokens when T is small, else on a slice of tokens scaled by T
+    sub = min(shape.T, 512)
     Y = np.random.default_rng(0).standard_normal((sub * shape.k, shape.H))
     t2 = time.perf_counter()
     omoe.combine(Y, np.arange(sub * shape.k), rw[:sub])
     t_comb = (time.perf_counter() - t2) * shape.T / sub
-    total = t_rp + t_experts + t_comb
-    return {"value": shape.T / total, "unit": "tokens/s", "cores": int(threads), "kind": "oracle",
-            "sample": (f"route+permute over all {shape.T} tokens ({t_rp:.1f}s); expert body (dequantise + "
-                       f"SwiGLU MLP, float64) on {len(samples)} of {len(hit)} hit experts at evenly spaced "
-                       f"row-count ranks ({', '.join(str(int(v)) for v in n)} rows), fitted t = a + b*rows "
-                       f"(a={a:.3f}s, b={b * 1e3:.3f}ms/row) and summed over all hit experts; combine timed "
-                       f"on {sub} tokens and scaled; est. whole-layer oracle time {total:.1f}s"),
-            "host_cpus": os.cpu_count()}
+    measured = len(samples) == len(hit)
+    return t_rp + t_exp + t_comb, measured, (f"route+permute over all {shape.T} tokens ({t_rp:.2f}s); expert "
+                                             f"body: {how}; combine " + ("timed on all tokens" if sub == shape.T
+                                             else f"timed on {sub} tokens and scaled to {shape.T}"))
+
+
+def cpu_baseline(shape, li, budget_s=20.0):
+    """The oracle as it stands, timed on this host's cores on a bounded piece of the workload
+    (about budget_s seconds of CPU work), reported as whole-layer tokens/s."""
+    host = host_info()
+    total, measured, how = _time_experts(shape, li, 0, budget_s)
+    reps = 1
+    if measured and total < 0.2:
+        # a layer of a few milliseconds: repeat it (weights regenerated untimed each time) and average
+        reps = int(min(200, max(1, 0.5 // max(total, 1e-4))))
+        total = float(np.mean([total] + [_time_experts(shape, li, 0, budget_s)[0] for _ in range(reps - 1)]))
+        how += f"; mean of {reps} repetitions"
+    return {"value": shape.T / total, "unit": "tokens/s", "cores": _blas_threads(host), "kind": "oracle",
+            "method": "whole layer timed" if measured else "extrapolated from a stratified sample of experts",
+            "sample": f"{how}; whole-layer oracle time {total * 1e3:.1f} ms", "host": host}
+
+
+def cpu_baseline_streamed(shape, budget_s=5.0, layers=(0, 1, 21, 42)):
+    """The oracle on layers {0, 1, 21, 42} of the stacked workload (each layer on the input it would get
+    if the previous one produced N(0,1) bf16 rows: the layer's cost does not depend on its input values),
+    plus the RMS rescale, scaled by num_layers / 4: an extrapolation, labelled as such."""
+    from oracle import moe as omoe
+    host = host_info()
+    L = shape.layers
+    per = []
+    notes = []
+    for l in layers:
+        if l >= L:
+            continue
+        li = gen.LayerInputs(shape, gen.activations_bf16(shape), gen.router_logits(shape, l))
+        t, measured, how = _time_experts(shape, li, l, budget_s)
+        y = np.random.default_rng(l).standard_normal((min(shape.T, 1024), shape.H))
+        t1 = time.perf_counter()
+        omoe.to_bf16_bits(omoe.rms_rescale(y))
+        t += (time.perf_counter() - t1) * shape.T / y.shape[0]
+        per.append(t)
+        notes.append(f"layer {l}: {t:.1f}s ({'all experts timed' if measured else 'expert sample'})")
+    total = float(np.mean(per)) * L
+    return {"value": shape.T / total, "unit": "tokens/s", "cores": _blas_threads(host), "kind": "oracle",
+            "method": f"extrapolated: mean of layers {list(layers)} x {L}",
+            "sample": "; ".join(notes) + f"; est. {L}-layer oracle time {total:.0f}s", "host": host}
+
+
+def hbm_read_peak(nbytes=4 << 30):
+    """Measured HBM stream-read bandwidth (libmxmoe_probe.so), best of a small launch-shape sweep over a
+    4 GiB buffer: the denominator beside the published 8 TB/s for weight-streaming shapes."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_weight_mixture_amd", "libmxmoe_probe.so"))
+    fn = lib.mxmoe_probe_stream_read
+    fn.restype = ctypes.c_float
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_void_p, ctypes.c_void_p]
+    buf = torch.empty(nbytes, dtype=torch.uint8, device="cuda")
+    buf.fill_(0x3C)
+    cus = torch.cuda.get_device_properties(0).multi_processor_count
+    out = torch.empty(cus * 32 * 256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    best, sweep = 0.0, {}
+    for per_cu in (4, 8, 16, 32):
+        ms = min(fn(buf.data_ptr(), nbytes, cus * per_cu, out.data_ptr(), stream) for _ in range(3))
+        if ms <= 0:
+            raise RuntimeError("stream-read probe failed")
+        gbps = nbytes / (ms * 1e-3) / 1e9
+        sweep[f"{per_cu}_blocks_per_cu"] = gbps
+        best = max(best, gbps)
+    del buf, out
+    torch.cuda.empty_cache()
+    return {"GBps": best, "bytes": nbytes, "sweep_GBps": sweep,
+            "kernel": "mxmoe_probe_stream_read (16-byte nontemporal loads, 8 in flight per thread)"}
 
 
 # --------------------------------------------------------------- workloads
@@ -272,6 +358,7 @@ def bench_layer(args):
     x_bf16 = li.x_bf16.to(dev)
     if shape.act == "mxfp8":
         x, xs = gen.quantize_mxfp8(x_bf16.float())      # input preparation, on the device
+        li.x_codes, li.x_scales = x.cpu(), xs.cpu()     # the same bytes for the CPU baseline
     else:
         x, xs = x_bf16, None
     logits = torch.from_numpy(li.logits).to(dev)
@@ -290,6 +377,8 @@ def bench_layer(args):
         torch.cuda.synchronize()
         torch.cuda.empty_cache()
         log(f"[bench] weights tiled at load in {time.time() - t0:.1f}s (cumulative)")
+    hbm = hbm_read_peak()
+    log(f"[bench] HBM stream read: {hbm['GBps']:.0f} GB/s (best of {hbm['sweep_GBps']})")
     steps = Steps(shape, w, x, xs, logits, inter, w_format)
     steps.run()
     torch.cuda.synchronize()
@@ -342,7 +431,8 @@ def bench_layer(args):
         dbytes = fc1_w if dom == "fc1" else fc2_w
         roof = {"bound": "hbm", "achieved": dbytes / (dm * 1e-3) / 1e9, "peak": PEAK["hbm_GBps"], "unit": "GB/s",
                 "traffic": None, "kernel": f"{dom} grouped GEMM", "per_launch_ms": dm,
-                "algorithmic_per_launch": dbytes}
+                "algorithmic_per_launch": dbytes,
+                "measured_read_peak": hbm["GBps"], "frac_of_measured_read_peak": dbytes / (dm * 1e-3) / 1e9 / hbm["GBps"]}
     else:
         dm = fc1_ms if dom == "fc1" else fc2_ms
         dfl = fc1_flops if dom == "fc1" else fc2_flops
@@ -352,7 +442,7 @@ def bench_layer(args):
                 "traffic": None, "kernel": f"{dom} grouped GEMM", "per_launch_ms": dm,
                 "algorithmic_per_launch": dfl}
     roof["frac"] = roof["achieved"] / roof["peak"]
-    roof["traffic"] = measured_traffic(name, inter, dom, w_format, T)
+    roof["traffic"], roof["traffic_source"] = measured_traffic(shape, inter, dom, w_format)
     rec = {
         "metric": METRIC,
         "value": T / (ms * 1e-3),
@@ -374,6 +464,8 @@ def bench_layer(args):
         "tflops": tflops,
         "pct_mxfp4_peak": tflops / PEAK["mxfp4_TFLOPs"],
         "hbm_algorithmic_GBps": alg_bytes / (ms * 1e-3) / 1e9,
+        "hbm_algorithmic_frac_of_8TBps": alg_bytes / (ms * 1e-3) / 1e9 / PEAK["hbm_GBps"],
+        "hbm_read_peak": hbm,
         "step_split_ms": dict(zip(Steps.NAMES, [float(v) for v in split])),
         "wall_ms_per_step": t_wall / args.steps * 1e3,
         "roofline": roof,
@@ -407,10 +499,27 @@ def _gemm_call(kernel_name):
     return None
 
 
+def _traffic_key(shape, inter, w_format):
+    """What a traffic record must match to describe this run: the sources of the kernels that decide the
+    grouped GEMM's work (the GEMM itself, routing and permutation), the input generator, and the workload."""
+    srcs = {}
+    for rel in ("mxfp4_weight_mixture_amd/csrc/gemm.hip", "mxfp4_weight_mixture_amd/csrc/route.hip",
+                "mxfp4_weight_mixture_amd/csrc/permute.hip", "workloads/gen.py"):
+        srcs[rel] = hashlib.sha256(open(os.path.join(ROOT, rel), "rb").read()).hexdigest()[:16]
+    return {"sources_sha256_16": srcs, "workload": dataclasses.asdict(shape), "intermediate_dtype": inter,
+            "weight_format": w_format}
+
+
+def _traffic_path(shape, name):
+    return os.path.join(ROOT, "profiles", f"gemm_traffic_{name}" + (f"_t{shape.T}" if name == "decode" else "")
+                        + ".json")
+
+
 def write_traffic_record(args):
     """HBM bytes per FC1 / FC2 call from FETCH_SIZE and WRITE_SIZE (KiB per dispatch), each scaled by
     what the same counter reads for a device add of 1 GiB in and 1 GiB out (bench.py --copy-calibration).
     A call is one launch per row-tile class, so a call's bytes are the sum of the class kernels' means."""
+    import subprocess
     name = args.workload
     shape = gen.preset(name, **({"T": args.tokens} if args.tokens else {}))
     inter = args.inter or ("mxfp8" if shape.act == "mxfp8" and shape.H % 512 == 0 else "bf16")
@@ -422,9 +531,13 @@ def write_traffic_record(args):
         cal = [v for k, vals in _counter_rows(os.path.join(d, f"cal_{ctr}")).items()
                if "elementwise" in k and "_add" in k for v in vals]
         scale[ctr] = (1 << 30) / 1024 / float(np.mean(cal))
-    rec = {"workload": name, "T": shape.T, "intermediate_dtype": inter, "weight_format": w_format,
-           "gemm_source_sha256": hashlib.sha256(open(os.path.join(ROOT, "mxfp4_weight_mixture_amd", "csrc",
-                                                                   "gemm.hip"), "rb").read()).hexdigest()}
+    try:
+        head = subprocess.run(["git", "-C", ROOT, "rev-parse", "--short=12", "HEAD"], capture_output=True,
+                              text=True).stdout.strip() or None
+    except OSError:
+        head = None
+    rec = {"workload": name, "T": shape.T, "key": _traffic_key(shape, inter, w_format),
+           "counters_dir": os.path.relpath(os.path.abspath(d), ROOT), "head_when_recorded": head}
     per_kernel = {}
     for ctr, key in (("FETCH_SIZE", "read"), ("WRITE_SIZE", "write")):
         for kname, vals in _counter_rows(os.path.join(d, f"pmc_{ctr}")).items():
@@ -440,30 +553,28 @@ def write_traffic_record(args):
         rec[f"{call}_bytes"] = rec.get(f"{call}_read_bytes", 0.0) + rec.get(f"{call}_write_bytes", 0.0)
     rec["scale"] = scale
     rec["per_kernel"] = per_kernel
-    out = os.path.join(ROOT, "profiles", f"gemm_traffic_{name}" + (f"_t{shape.T}" if name == "decode" else "")
-                       + ".json")
+    out = _traffic_path(shape, name)
     json.dump(rec, open(out, "w"), indent=1)
     print(json.dumps({k: v for k, v in rec.items() if k != "per_kernel"}))
 
 
-def measured_traffic(workload, inter, call, w_format, T=None):
-    """HBM bytes (FETCH_SIZE + WRITE_SIZE, scaled by the copy-kernel calibration)
-    of one `call` ("fc1"/"fc2"), as the rocprofv3 counter runs under profiles/
-    recorded them, or None when there is no record for this workload or the
-    grouped-GEMM source has changed since it was taken."""
-    path = os.path.join(ROOT, "profiles", f"gemm_traffic_{workload}" + (f"_t{T}" if workload == "decode" else "")
-                        + ".json")
+def measured_traffic(shape, inter, call, w_format):
+    """(HBM bytes of one `call` ("fc1"/"fc2") from the rocprofv3 counter record under profiles/, source)
+    or (None, reason) when there is no record for this workload or anything in its key -- the GEMM,
+    routing and permutation sources, the input generator, the workload, the intermediate precision or
+    the weight format -- differs from this run."""
+    name = next((n for n, s in gen.PRESETS.items() if dataclasses.replace(s, T=shape.T) == shape), None)
+    if name is None:
+        return None, "no record for this workload"
+    path = _traffic_path(shape, name)
     if not os.path.exists(path):
-        return None
+        return None, f"no record ({os.path.relpath(path, ROOT)})"
     rec = json.load(open(path))
-    if T is not None and rec.get("T", T) != T:
-        return None
-    src = os.path.join(ROOT, "mxfp4_weight_mixture_amd", "csrc", "gemm.hip")
-    sha = hashlib.sha256(open(src, "rb").read()).hexdigest()
-    if rec.get("gemm_source_sha256") != sha or rec.get("intermediate_dtype") != inter \
-            or rec.get("weight_format", "canonical") != w_format:
-        return None
-    return rec.get(f"{call}_bytes")
+    if rec.get("key") != _traffic_key(shape, inter, w_format):
+        return None, f"{os.path.relpath(path, ROOT)} was taken on other sources or another workload"
+    return rec.get(f"{call}_bytes"), {"record": os.path.relpath(path, ROOT),
+                                      "head_when_recorded": rec.get("head_when_recorded"),
+                                      "counters_dir": rec.get("counters_dir")}
 
 
 def bench_graph(shape, w, x, xs, logits, inter, args, w_format="canonical"):
@@ -708,10 +819,14 @@ def main():
         return
     if args.workload == "streamed":
         rec = bench_streamed(args)
+        if not args.no_cpu_baseline:
+            shape = gen.preset("streamed", **({"T": args.tokens} if args.tokens else {}))
+            rec["cpu_baseline"] = cpu_baseline_streamed(shape)
+            log(f"[bench] cpu baseline: {rec['cpu_baseline']}")
     else:
         rec, shape, li, ids = bench_layer(args)
         if not args.no_cpu_baseline:
-            rec["cpu_baseline"] = cpu_baseline(shape, li, ids)
+            rec["cpu_baseline"] = cpu_baseline(shape, li)
             log(f"[bench] cpu baseline: {rec['cpu_baseline']}")
     print(json.dumps(rec))
 

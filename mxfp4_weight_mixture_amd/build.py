@@ -20,8 +20,9 @@ PKG = os.path.dirname(os.path.abspath(__file__))
 ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 LIB = os.path.join(PKG, "libmxmoe.so")
-# measurement tooling (matrix-instruction issue rates), a library of its own outside libmxmoe's ABI
-PROBE_SRC = os.path.join(PKG, "probe", "mfma_rate.hip")
+# measurement tooling (matrix-instruction issue rates, HBM stream read), a library of its own
+# outside libmxmoe's ABI
+PROBE_DIR = os.path.join(PKG, "probe")
 PROBE_LIB = os.path.join(PKG, "libmxmoe_probe.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
@@ -64,7 +65,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, LIB)
     tmp = PROBE_LIB + ".tmp"
-    cmd = [hipcc(), *CXXFLAGS, "-shared", PROBE_SRC, "-o", tmp]
+    cmd = [hipcc(), *CXXFLAGS, "-shared", *sorted(glob.glob(os.path.join(PROBE_DIR, "*.hip"))), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"building the probe failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")

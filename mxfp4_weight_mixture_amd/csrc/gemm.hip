@@ -391,17 +391,19 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
 // 16 different 16-byte bank groups, and any 8 consecutive rows 8 different
 // ones, with no padding.
 
-// Waves per block.  The full FP8 tile of FC1 runs eight (two per SIMD, each
-// wave a 64x128 slice): measured faster than four 128x128 waves for FC1.
-// FC2's (bf16 output staged through LDS) spills at eight and stays at four.
+// Waves per block.  The full FP8 tiles run eight (two per SIMD, each wave a
+// 64x128 slice): measured faster than four 128x128 waves.  The full bf16
+// tile (128 rows) runs eight waves of 64x64: with four, one wave per SIMD
+// both expands the FP4 weights to bf16 on the vector ALU and feeds the
+// matrix core.
 template <int BM, bool FP8, int EPI>
-constexpr int dma_waves() { return (BM == 256 && FP8 && EPI != 0) ? 8 : 4; }
+constexpr int dma_waves() { return ((BM == 256 && FP8) || (BM == 128 && !FP8)) ? 8 : 4; }
 
 template <int BM, bool FP8, int NWAVES = 4>
 struct Cfg2 {
   static constexpr int NW = NWAVES;
   static constexpr int NT = NW * 64;
-  static constexpr int WAVES_M = NW == 8 ? 4 : (BM >= 128 ? 2 : 1);
+  static constexpr int WAVES_M = NW == 8 ? (BM == 256 ? 4 : 2) : (BM >= 128 ? 2 : 1);
   static constexpr int WAVES_N = NW / WAVES_M;
   static constexpr int WM = BM / WAVES_M;
   static constexpr int WN = kBN / WAVES_N;
@@ -547,9 +549,13 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
     const int g = lane >> 5;
     // 32-column block of the tile that B fragment j of this wave reads.  Tile
     // columns come in groups of 64 (32 gate rows, then their 32 up rows) for
-    // every tile class; with a SwiGLU epilogue the wave's fragments are ordered
-    // gate blocks first, so that fragment fh and fh + FN/2 pair up.
-    auto frag_block = [](int j) { return EPI == 0 ? j : (j % (C::FN / 2)) * 2 + j / (C::FN / 2); };
+    // every tile class; the wave's fragments are ordered even blocks first, so
+    // that with a SwiGLU epilogue fragment fh (gate) and fh + FN/2 (up) pair
+    // up.  Without one the epilogue writes the same pairs side by side: that
+    // order is also what keeps the eight-wave FC2 tile free of spills (its
+    // identity order spilled 24-33 VGPRs of DMA offsets and LDS addresses
+    // inside the K loop).
+    auto frag_block = [](int j) { return (j % (C::FN / 2)) * 2 + j / (C::FN / 2); };
     // fragment rows / lines start at multiples of 16, so the swizzles depend on the lane only
     const int xa = a_swz<FP8>(l32 & 15);
     const int xb = b_swz((l32 >> 1) & 7);
@@ -937,19 +943,34 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
     // gate/up pairing of the SwiGLU layouts: fragment fh holds the gate columns
     // of 32-column block 2fh, fragment fh + FN/2 the matching up columns of
     // block 2fh + 1 (see frag_block)
+    {
+    // The epilogue's lane-derived values come from a fresh opaque copy of the
+    // thread index: derived from the one above, its store addresses were
+    // computed ahead of the K loop and kept live through it, which pushed the
+    // eight-wave FC1 tile into spills.
+    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
+    const int lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm0 = (wave / C::WAVES_N) * C::WM;
+    const int wn0 = (wave % C::WAVES_N) * C::WN;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
     constexpr int HF = C::FN / 2;
     if constexpr (OUT == MOE_OUT_FP32) {
       // fp32: straight from the accumulators, one fragment at a time
       if constexpr (EPI == 0) {
+        // fragment fh holds 32-column block 2fh, fragment fh + FN/2 block 2fh + 1
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) {
-            const int n = nt * kBN + wn0 + fn * 32 + l32;
+          for (int fh = 0; fh < HF; ++fh) {
+            const int n = nt * kBN + wn0 + 2 * fh * 32 + l32;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
               const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              if (r < mrows && n < p.N) static_cast<float*>(p.c)[(size_t)(row0 + r) * p.N + n] = acc[fm][fn][q];
+              float* const crow = static_cast<float*>(p.c) + (size_t)(row0 + r) * p.N;
+              if (r < mrows && n < p.N) crow[n] = acc[fm][fh][q];
+              if (r < mrows && n + 32 < p.N) crow[n + 32] = acc[fm][fh + HF][q];
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -980,15 +1001,18 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
       static_assert(BM * PITCH <= C::LDS_TOTAL, "C tile must fit in LDS");
       stage_barrier();   // every wave is done reading the stage buffers
       if constexpr (EPI == 0) {
+        // fragment fh holds 32-column block 2fh, fragment fh + FN/2 block 2fh + 1
 #pragma unroll
         for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) {
-            uint8_t* col = lds + (wn0 + fn * 32 + l32) * 2;
+          for (int fh = 0; fh < HF; ++fh) {
+            uint8_t* col = lds + (wn0 + 2 * fh * 32 + l32) * 2;
 #pragma unroll
             for (int q = 0; q < 16; ++q) {
               const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)acc[fm][fn][q];   // v_cvt_pk_bf16_f32 (RNE)
+              // v_cvt_pk_bf16_f32 (RNE)
+              *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)acc[fm][fh][q];
+              *reinterpret_cast<__bf16*>(col + 64 + r * PITCH) = (__bf16)acc[fm][fh + HF][q];
             }
             __builtin_amdgcn_sched_barrier(0);
           }
@@ -1067,6 +1091,7 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
           osc[(size_t)r * (ld / 32) + c / 32] = (uint8_t)(x + 127);
         }
       }
+    }
     }
     // every wave is done with LDS before the next unit refills it
     stage_barrier();
