@@ -3,8 +3,10 @@
 //   out[t][h] = sum_{j ascending} w[t][j] * y[dest_row[t*k + j]][h]   (fp32)
 // One workgroup per token; each thread owns 8 consecutive h (16-byte bf16
 // or 32-byte fp32 loads), so every row of y is read once, coalesced, and
-// no atomics are involved.  Optionally also writes the next stacked layer's
-// input bf16(out[t] / rms(out[t])).
+// no atomics are involved.  The workgroup is sized to the row (at most 512
+// threads, whole waves, every pass over the row full but the last), and a
+// thread has up to 16 rows of y in flight.  Optionally also writes the next
+// stacked layer's input bf16(out[t] / rms(out[t])).
 #include "internal.h"
 
 namespace mxmoe {
@@ -42,12 +44,22 @@ __device__ inline uint32_t bf16_rne(float f) {
 
 // Rows are fetched kBatch at a time before any is accumulated (more loads in
 // flight per thread); the accumulation order stays j = 0, 1, ..., k-1.
-constexpr int kBatch = 8;
-constexpr int kThreads = 256;   // threads per token
-constexpr int kWaves = kThreads / 64;
+constexpr int kBatch = 16;
+constexpr int kMaxThreads = 512;   // threads per token, at most
+constexpr int kMaxWaves = kMaxThreads / 64;
+
+// Threads per token for rows of H elements: the fewest passes of at most
+// kMaxThreads threads over the H/8 vectors, then the fewest whole waves that
+// cover a pass.
+int combine_threads(int H) {
+  const int nv = H / 8;
+  const int passes = (nv + kMaxThreads - 1) / kMaxThreads;
+  const int per_pass = (nv + passes - 1) / passes;
+  return (per_pass + 63) / 64 * 64;
+}
 
 template <typename YT>
-__global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict__ y,
+__global__ __launch_bounds__(kMaxThreads) void combine_kernel(const YT* __restrict__ y,
                                                       const int32_t* __restrict__ dest_row,
                                                       const float* __restrict__ w, int k, int H,
                                                       float* __restrict__ out,
@@ -58,8 +70,9 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict_
   float* orow = out + (size_t)t * H;
   const int32_t* rows = dest_row + (size_t)t * k;
   const float* wt = w + (size_t)t * k;
+  const int nthr = blockDim.x;
   float ss = 0.f;
-  for (int v = threadIdx.x; v < nv; v += kThreads) {
+  for (int v = threadIdx.x; v < nv; v += nthr) {
     float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
     for (int j0 = 0; j0 < k; j0 += kBatch) {
       Raw raw[kBatch];
@@ -83,17 +96,16 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict_
     for (int i = 0; i < 8; ++i) ss = fmaf(acc[i], acc[i], ss);
   }
   if (x_next == nullptr) return;  // uniform over the block
-  __shared__ float red[kWaves];
+  __shared__ float red[kMaxWaves];
 #pragma unroll
   for (int off = 32; off > 0; off >>= 1) ss += __shfl_xor(ss, off, 64);
   if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = ss;
   __syncthreads();
   float tot = 0.f;
-#pragma unroll
-  for (int i = 0; i < kWaves; ++i) tot += red[i];
+  for (int i = 0; i < nthr / 64; ++i) tot += red[i];
   const float inv = 1.0f / sqrtf(tot / (float)H);
   uint16_t* xrow = x_next + (size_t)t * H;
-  for (int v = threadIdx.x; v < nv; v += kThreads) {
+  for (int v = threadIdx.x; v < nv; v += nthr) {
     float o[8];
     load8(orow + 8 * v, o);  // this thread's own writes
     uint4 q;
@@ -110,11 +122,12 @@ __global__ __launch_bounds__(kThreads) void combine_kernel(const YT* __restrict_
 moe_status launch_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* w,
                           int T, int k, int H, float* out, uint16_t* x_next, hipStream_t s) {
   if (T == 0) return MOE_OK;
+  const int threads = combine_threads(H);
   if (y_dtype == MOE_OUT_BF16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(T), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(T), dim3(threads), 0, s,
                        static_cast<const uint16_t*>(y), dest_row, w, k, H, out, x_next);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(kThreads), 0, s,
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(threads), 0, s,
                        static_cast<const float*>(y), dest_row, w, k, H, out, x_next);
   MXMOE_HIP(hipGetLastError());
   return MOE_OK;

@@ -75,6 +75,7 @@ struct Params {
   const Tile* tiles;
   const int32_t* tile_count;
   int32_t* unit_ctr;          // [8] per-XCD unit counters of this launch (zeroed by the planner)
+  int tile_cap;               // the mixed launch: stride between the classes' tile lists
   int a_gather_div;
   int N, K, n_out, n_tiles;
   int layout;  // 0 none, 1 split, 2 interleaved
@@ -506,6 +507,582 @@ __device__ inline int mxfp8_block_exp(float amax) {
 // one barrier in the middle of each stage that both publishes stage s+1 and
 // frees stage s's buffer for the DMA of stage s+3.  bf16 operands: the
 // stage's reads and products follow one barrier at its start.
+// One unit (row tile x 256-column n-tile) of a grouped GEMM class: the DMA
+// pipeline over K and the epilogue.  tid_in: the thread's index within the
+// NW waves that run the unit; lds: their LDS area (Cfg2<BM, FP8, NW>::LDS_TOTAL
+// bytes); store: false runs the unit without writing C (a block that runs two
+// units side by side keeps both halves in step with one).  Every wave of the
+// block executes the same barriers.
+template <int BM, bool FP8, int EPI, int OUT, bool TILED, int NW>
+__device__ __forceinline__ void run_unit(const Params& p, int u, int count, int tid_in, uint8_t* lds, bool store) {
+  using C = Cfg2<BM, FP8, NW>;
+  const int K = p.K;
+  const int a_row_bytes = FP8 ? K : 2 * K;
+  const int kb = K / 32;
+  const int nst = K / C::KS;
+
+  // Lane-derived values are recomputed per unit from an opaque copy of the
+  // thread index.  Hoisted out of the unit loop they stay live across it and
+  // get spilled, and a spill reload in the pipeline prologue would wait for
+  // every DMA in flight.
+  int tid;
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid_in));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave / C::WAVES_N) * C::WM;
+  const int wn0 = (wave % C::WAVES_N) * C::WN;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  // 32-column block of the tile that B fragment j of this wave reads.  Tile
+  // columns come in groups of 64 (32 gate rows, then their 32 up rows) for
+  // every tile class; the wave's fragments are ordered even blocks first, so
+  // that with a SwiGLU epilogue fragment fh (gate) and fh + FN/2 (up) pair
+  // up.  Without one the epilogue writes the same pairs side by side: that
+  // order is also what keeps the eight-wave FC2 tile free of spills (its
+  // identity order spilled 24-33 VGPRs of DMA offsets and LDS addresses
+  // inside the K loop).
+  auto frag_block = [](int j) { return (j % (C::FN / 2)) * 2 + j / (C::FN / 2); };
+  // fragment rows / lines start at multiples of 16, so the swizzles depend on the lane only
+  const int xa = a_swz<FP8>(l32 & 15);
+  const int xb = b_swz((l32 >> 1) & 7);
+
+  // units in groups of up to 4 row tiles x all n-tiles, row tile fastest, so
+  // that concurrent blocks of one XCD share both their A rows and their B tiles
+  constexpr int GM = 4;
+  const int grp = u / (GM * p.n_tiles);
+  const int first = grp * GM;
+  const int gsize = min(GM, count - first);
+  const int in = u - grp * GM * p.n_tiles;
+  const int ti = first + in % gsize;
+  const int nt = in / gsize;
+  const Tile tile = p.tiles[ti];
+  const int e = tile.expert;
+  const int row0 = tile.row0;
+  const int mrows = min(BM, p.offsets[e + 1] - row0);
+  const size_t w_expert = (size_t)e * p.N;
+
+  // ---- DMA sources: uniform bases, 32-bit per-lane byte offsets (stage 0) ----
+  // gathered A rows: offsets from the start of A; contiguous A rows: from the tile's first row
+  const bool gather = p.a_gather != nullptr;
+  const uint8_t* const a_base = gather ? p.a : p.a + (size_t)row0 * a_row_bytes;
+  uint32_t a_off[C::A_I];
+  {
+    int arow[C::A_I];
+#pragma unroll
+    for (int i = 0; i < C::A_I; ++i)
+      arow[i] = min((wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA, mrows - 1);
+    if (gather) {
+      // all index loads in flight together
+#pragma unroll
+      for (int i = 0; i < C::A_I; ++i) arow[i] = p.a_gather[row0 + arow[i]];
+#pragma unroll
+      for (int i = 0; i < C::A_I; ++i) arow[i] /= p.a_gather_div;
+    }
+#pragma unroll
+    for (int i = 0; i < C::A_I; ++i) {
+      const int r = (wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA;
+      const int chunk = (lane % C::SA) ^ a_swz<FP8>(r);
+      a_off[i] = (uint32_t)arow[i] * (uint32_t)a_row_bytes + chunk * 16;
+    }
+  }
+  // B: canonical weights are addressed row by row (tile column j of the
+  // stage's LDS layout <- its weight row); tiled weights already hold the
+  // stage's 16 KB in LDS order, so each instruction copies 1 KB of
+  // consecutive bytes.  b_step / bs_step: bytes from one stage (one scale
+  // group) to the next.
+  const size_t tile_id = (size_t)e * p.n_tiles + nt;
+  const uint8_t* const b_base = TILED ? p.w + tile_id * (size_t)nst * C::LDS_B : p.w + w_expert * (size_t)(K / 2);
+  const int b_step = TILED ? C::LDS_B : C::RB;
+  uint32_t b_off[C::B_I];
+#pragma unroll
+  for (int i = 0; i < C::B_I; ++i) {
+    const int line = (wave * C::B_I + i) * 8 + lane / 8;
+    const int uu = (lane & 7) ^ b_swz(line);
+    const int j = line * 2 + (uu >> 2);
+    const int wr = w_row_of<kSwiGroup>(p.layout, nt, j, p.N, p.n_out);
+    b_off[i] = TILED ? (uint32_t)((wave * C::B_I + i) * 1024 + lane * 16)
+                         : (uint32_t)wr * (uint32_t)(K / 2) + (uu & 3) * 16;
+  }
+  // scale loads: with four waves every wave loads 64 rows of A scales (if
+  // below BM) and 64 of B scales; with eight, waves 0-3 load A, 4-7 load B
+  const bool a_sw = C::NW == 8 ? wave < 4 : true;
+  const bool b_sw = C::NW == 8 ? wave >= 4 : true;
+  const int sw = (C::NW == 8 && wave >= 4) ? wave - 4 : wave;
+  const int srow = sw * 64 + lane;   // scale row this lane loads (A: if < BM)
+  const uint8_t* const as_base = gather ? p.a_scales : p.a_scales + (size_t)row0 * kb;
+  uint32_t as_off = 0;
+  if (FP8 && a_sw && srow < BM) {
+    const int r = min(srow, mrows - 1);
+    as_off = (uint32_t)(gather ? p.a_gather[row0 + r] / p.a_gather_div : r) * (uint32_t)kb;
+  }
+  const uint8_t* const bs_base =
+      TILED ? p.w_scales + tile_id * (size_t)(K / 512) * 4096 : p.w_scales + w_expert * (size_t)kb;
+  const int bs_step = TILED ? 4096 : 16;
+  const uint32_t bs_off = TILED ? (uint32_t)(sw * 1024 + lane * 16)
+                                    : (uint32_t)w_row_of<kSwiGroup>(p.layout, nt, srow, p.N, p.n_out) * (uint32_t)kb;
+  uint8_t* const sg = lds + C::NST * C::LDS_STAGE;   // two scale groups
+
+  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
+  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
+  const __amdgpu_buffer_rsrc_t ras = make_rsrc(as_base);
+  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(bs_base);
+  auto issue = [&](int s) {
+    uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
+#pragma unroll
+    for (int i = 0; i < C::A_I; ++i) dma16(ra, a_off[i], s * C::RA, base + (wave * C::A_I + i) * 1024);
+#pragma unroll
+    for (int i = 0; i < C::B_I; ++i)
+      dma16(rb, b_off[i], s * b_step, base + C::LDS_A + (wave * C::B_I + i) * 1024);
+  };
+  // DMA instruction j of stage s (j < A_I: A, then B), for interleaving with products
+  auto issue_one = [&](int s, int j) {
+    uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
+    if (j < C::A_I) dma16(ra, a_off[j], s * C::RA, base + (wave * C::A_I + j) * 1024);
+    else dma16(rb, b_off[j - C::A_I], s * b_step, base + C::LDS_A + (wave * C::B_I + j - C::A_I) * 1024);
+  };
+  // scale group j (stages 4j..4j+3): 16 bytes of every A and B row
+  auto issue_scales = [&](int j) {
+    uint8_t* base = sg + (j & 1) * C::LDS_SG;
+    // (a 32-row tile has 512 bytes of A scales per group: lanes 32-63 stay idle)
+    if (FP8 && a_sw && sw * 64 < BM && (BM >= 64 || lane < BM)) dma16(ras, as_off, 16 * j, base + sw * 1024);
+    if (b_sw) dma16(rbs, bs_off, bs_step * j, base + C::SG_A + sw * 1024);
+  };
+
+  v16f acc[C::FM][C::FN];
+#pragma unroll
+  for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+    for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+  if constexpr (FP8) {
+    uint32_t sa[C::FM], sb[C::FN], na[C::FM], nb[C::FN];
+    v8i a0[C::FM], a1[C::FM];
+    v4i b0[C::FN], b1[C::FN];
+    // LDS base of stage s, made opaque to the compiler: otherwise every
+    // fragment address becomes an induction variable of its own
+    auto stage_lds = [&](int s) {
+      return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
+    };
+    // read j of one k-half: j < FN: B fragment j; then the A fragments' low and high halves
+    // (A: K [kk*64 + 16g, +16) and [kk*64 + 32 + 16g, +16) = chunks 4kk+g and 4kk+2+g)
+    auto read_frag = [&](int s, int kk, int j, v8i (&af)[C::FM], v4i (&bq)[C::FN]) {
+      const uint8_t* la = stage_lds(s);
+      if (j < C::FN) {
+        const int n = wn0 + frag_block(j) * 32 + l32;
+        const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xb;
+        bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
+      } else {
+        const int fm = (j - C::FN) >> 1, hi = (j - C::FN) & 1;
+        const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
+        const v4i v = *reinterpret_cast<const v4i*>(row + (((4 * kk + 2 * hi + g) ^ xa) << 4));
+        if (hi) {
+          af[fm][4] = v[0]; af[fm][5] = v[1]; af[fm][6] = v[2]; af[fm][7] = v[3];
+        } else {
+          af[fm][0] = v[0]; af[fm][1] = v[1]; af[fm][2] = v[2]; af[fm][3] = v[3];
+        }
+      }
+    };
+    // scale word j of stage s: four E8M0 bytes (the stage's blocks) of an A row or B column
+    auto read_scale = [&](int s, int j, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
+      const uint8_t* lsg = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4);
+      if (j < C::FM) ta[j] = *reinterpret_cast<const uint32_t*>(lsg + (wm0 + j * 32 + l32) * 16);
+      else tb[j - C::FM] = *reinterpret_cast<const uint32_t*>(lsg + C::SG_A + (wn0 + frag_block(j - C::FM) * 32 + l32) * 16);
+    };
+    // product i of one k-half, B-fragment major.  ta/tb hold this lane's scale
+    // bytes in the order the op_sel field reads them: byte kk = block 2kk + g.
+    auto mma = [&](int kk, int i, const v8i (&af)[C::FM], const v4i (&bq)[C::FN], const uint32_t (&ta)[C::FM],
+                   const uint32_t (&tb)[C::FN]) {
+      const int fn = i / C::FM, fm = i % C::FM;
+      const v8i bf = v8i{bq[fn][0], bq[fn][1], bq[fn][2], bq[fn][3], 0, 0, 0, 0};
+      if (kk == 0)
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0 /*A: fp8 e4m3*/,
+                                                                      4 /*B: fp4 e2m1*/, 0, ta[fm], 0, tb[fn]);
+      else
+        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0, 4, 1, ta[fm],
+                                                                      1, tb[fn]);
+    };
+    // a stage's four scale bytes (blocks 0..3) -> this lane's two, in op_sel order
+    const uint32_t scale_sel = g ? 0x0c0c0301u : 0x0c0c0200u;
+    auto order_scales = [&](uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
+#pragma unroll
+      for (int j = 0; j < C::FM; ++j) ta[j] = __builtin_amdgcn_perm(0u, ta[j], scale_sel);
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j) tb[j] = __builtin_amdgcn_perm(0u, tb[j], scale_sel);
+    };
+    constexpr int MF = C::FM * C::FN;
+    constexpr int NR = 2 * C::FM + C::FN;   // fragment reads of one k-half
+    constexpr int NS = C::FM + C::FN;       // scale reads of one stage
+    // reads issued after each product: at least two (front-loaded), more for small tiles
+    constexpr int R1 = (NR + MF - 1) / MF > 2 ? (NR + MF - 1) / MF : 2;
+    constexpr int R2 = (NR + NS + MF - 1) / MF > 2 ? (NR + NS + MF - 1) / MF : 2;
+    constexpr int D2 = (C::LOADS + MF - 1) / MF;   // refill DMA instructions per product
+    // One stage.  ISSUE: refill the freed buffer with stage s+3 during the second
+    // half (SCALES: and the next scale group); WAIT: vmcnt allowance at the
+    // mid-stage barrier, -1 for the last stage (no barrier, no next-stage
+    // reads).  All three are compile-time constants so that the loop body has
+    // no branch the compiler could sink the first half's products past.  Every
+    // group of one product and its reads / DMA is fenced with sched_barrier to
+    // keep the interleave.
+    auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN],
+                    uint32_t (&tna)[C::FM], uint32_t (&tnb)[C::FN]) {
+      constexpr bool kIssue = decltype(ISSUE)::value;
+      constexpr bool kScales = decltype(SCALES)::value;
+      constexpr int kWait = decltype(WAIT)::value;
+      order_scales(ta, tb);
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        mma(0, i, a0, b0, ta, tb);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int r = R1 * i; r < R1 * i + R1; ++r)
+          if (r < NR) read_frag(s, 1, r, a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      // the first half's products stay ahead of the barrier
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
+      if constexpr (kWait >= 0) {
+        // stage s fully read by this wave; stage s+1 landed for this wave's loads
+        wait_lgkm0();
+        wait_vm<kWait>();
+        stage_barrier();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        mma(1, i, a1, b1, ta, tb);
+        __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kWait >= 0) {
+#pragma unroll
+          for (int r = R2 * i; r < R2 * i + R2; ++r) {
+            if (r < NS) read_scale(s + 1, r, tna, tnb);
+            else if (r < NS + NR) read_frag(s + 1, 0, r - NS, a0, b0);
+          }
+        }
+        // the refill of the freed buffer (stage s+3), spread over the products
+        if constexpr (kIssue) {
+#pragma unroll
+          for (int j = D2 * i; j < D2 * i + D2; ++j) {
+            if (j < C::LOADS) issue_one(s + 3, j);
+            if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
+          }
+        }
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    using WL = std::integral_constant<int, C::LOADS>;   // stage s+2 may still be in flight
+    issue_scales(0);
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_vm<2 * C::LOADS>();
+    stage_barrier();
+#pragma unroll
+    for (int r = 0; r < NS; ++r) read_scale(0, r, sa, sb);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_frag(0, 0, r, a0, b0);
+    // the stage count is a multiple of four (K % 512 == 0): groups of four stages,
+    // the last group with its tail conditions resolved at compile time
+    int s = 0;
+    for (; s + 4 < nst; s += 4) {
+      step(s, T{}, F{}, WL{}, sa, sb, na, nb);
+      step(s + 1, T{}, T{}, WL{}, na, nb, sa, sb);
+      step(s + 2, T{}, F{}, WL{}, sa, sb, na, nb);
+      step(s + 3, T{}, F{}, WL{}, na, nb, sa, sb);
+    }
+    step(s, T{}, F{}, WL{}, sa, sb, na, nb);
+    step(s + 1, F{}, F{}, WL{}, na, nb, sa, sb);
+    step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sa, sb, na, nb);
+    step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, na, nb, sa, sb);
+  } else {
+    // bf16 A: the same pipeline as the FP8 path, with k-halves of 64 elements
+    // (block h of each lane half), the weights expanded to bf16 in registers
+    // (one conversion unit = 8 weights of one column, 4 instructions) spread
+    // over the products of the preceding 16-element step
+    uint32_t sb[C::FN], nb[C::FN];
+    v4i bqc[C::FN], bqn[C::FN];            // raw FP4 B of the current / next k-half
+    v8bf afc[4][C::FM], afn[4][C::FM];     // A of the current / next k-half, per 16-element step
+    v8bf bw[C::FN][4];                     // B of the current k-half, expanded
+    auto stage_lds = [&](int s) {
+      return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
+    };
+    // read j of k-half h: j < FN: raw B of column fragment j; then A (step, fm)
+    auto read_frag = [&](int s, int h, int j, v4i (&bq)[C::FN], v8bf (&af)[4][C::FM]) {
+      const uint8_t* la = stage_lds(s);
+      if (j < C::FN) {
+        const int n = wn0 + frag_block(j) * 32 + l32;
+        const int uu = ((n & 1) * 4 + 2 * h + g) ^ xb;
+        bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
+      } else {
+        const int s4 = (j - C::FN) / C::FM, fm = (j - C::FN) % C::FM;
+        const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
+        // bytes 128h + 64g + 16*s4 of the 256-byte stage row: slot 8h + 4g + s4
+        af[s4][fm] = *reinterpret_cast<const v8bf*>(row + (((8 * h + 4 * g + s4) ^ xa) << 4));
+      }
+    };
+    auto read_scale = [&](int s, int j, uint32_t (&tb)[C::FN]) {
+      const uint8_t* lsb = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4) + C::SG_A;
+      tb[j] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + frag_block(j) * 32 + l32) * 16);
+    };
+    // conversion unit (fn, d): the 8 weights of bw[fn][d] (E2M1 x block scale -> bf16, exact)
+    auto expand = [&](int h, int fn, int d, const v4i (&bq)[C::FN], const uint32_t (&tb)[C::FN]) {
+      const float sc = e8m0_to_f32((tb[fn] >> (8 * (2 * h + g))) & 0xff);
+      const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 0);
+      const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 1);
+      const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 2);
+      const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 3);
+      bw[fn][d] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    };
+    constexpr int MG = C::FN * C::FM;      // products of one 16-element step
+    constexpr int MF = 4 * MG;             // products of one k-half
+    constexpr int NR = C::FN + 4 * C::FM;  // reads of one k-half
+    constexpr int NS = C::FN;              // scale reads of one stage
+    constexpr int R1 = (NR + MF - 1) / MF > 1 ? (NR + MF - 1) / MF : 1;
+    constexpr int R2 = (NR + NS + MF - 1) / MF > 1 ? (NR + NS + MF - 1) / MF : 1;
+    constexpr int D2 = (C::LOADS + MF - 1) / MF;
+    // the products of k-half h from af/bq, with the expansion of step t+1's
+    // weights after the MFMAs of step t (unit fn after the step's product fn*FM),
+    // and EXTRA(i) (reads / DMA) after product i
+    auto half = [&](int h, const v4i (&bq)[C::FN], const v8bf (&af)[4][C::FM], const uint32_t (&tb)[C::FN],
+                    auto&& extra) {
+#pragma unroll
+      for (int fn = 0; fn < C::FN; ++fn) expand(h, fn, 0, bq, tb);
+#pragma unroll
+      for (int i = 0; i < MF; ++i) {
+        const int s4 = i / MG, fn = (i % MG) / C::FM, fm = i % C::FM;
+        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s4][fm], bw[fn][s4], acc[fm][fn], 0, 0, 0);
+        __builtin_amdgcn_sched_barrier(0);
+        if (s4 < 3 && fm == 0) expand(h, fn, s4 + 1, bq, tb);
+        extra(i);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+    };
+    auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&tb)[C::FN], uint32_t (&tnb)[C::FN]) {
+      constexpr bool kIssue = decltype(ISSUE)::value;
+      constexpr bool kScales = decltype(SCALES)::value;
+      constexpr int kWait = decltype(WAIT)::value;
+      half(0, bqc, afc, tb, [&](int i) {
+#pragma unroll
+        for (int r = R1 * i; r < R1 * i + R1; ++r)
+          if (r < NR) read_frag(s, 1, r, bqn, afn);
+      });
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
+      if constexpr (kWait >= 0) {
+        wait_lgkm0();
+        wait_vm<kWait>();
+        stage_barrier();
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      half(1, bqn, afn, tb, [&](int i) {
+        if constexpr (kWait >= 0) {
+#pragma unroll
+          for (int r = R2 * i; r < R2 * i + R2; ++r) {
+            if (r < NS) read_scale(s + 1, r, tnb);
+            else if (r < NS + NR) read_frag(s + 1, 0, r - NS, bqc, afc);
+          }
+        }
+        if constexpr (kIssue) {
+#pragma unroll
+          for (int j = D2 * i; j < D2 * i + D2; ++j) {
+            if (j < C::LOADS) issue_one(s + 3, j);
+            if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
+          }
+        }
+      });
+    };
+    using T = std::integral_constant<bool, true>;
+    using F = std::integral_constant<bool, false>;
+    using WL = std::integral_constant<int, C::LOADS>;
+    issue_scales(0);
+    issue(0);
+    issue(1);
+    issue(2);
+    wait_vm<2 * C::LOADS>();
+    stage_barrier();
+#pragma unroll
+    for (int r = 0; r < NS; ++r) read_scale(0, r, sb);
+#pragma unroll
+    for (int r = 0; r < NR; ++r) read_frag(0, 0, r, bqc, afc);
+    int s = 0;
+    for (; s + 4 < nst; s += 4) {
+      step(s, T{}, F{}, WL{}, sb, nb);
+      step(s + 1, T{}, T{}, WL{}, nb, sb);
+      step(s + 2, T{}, F{}, WL{}, sb, nb);
+      step(s + 3, T{}, F{}, WL{}, nb, sb);
+    }
+    step(s, T{}, F{}, WL{}, sb, nb);
+    step(s + 1, F{}, F{}, WL{}, nb, sb);
+    step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sb, nb);
+    step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, nb, sb);
+  }
+
+  // ---- epilogue: registers -> C in permuted row order ----
+  // gate/up pairing of the SwiGLU layouts: fragment fh holds the gate columns
+  // of 32-column block 2fh, fragment fh + FN/2 the matching up columns of
+  // block 2fh + 1 (see frag_block)
+  {
+  // The epilogue's lane-derived values come from a fresh opaque copy of the
+  // thread index: derived from the one above, its store addresses were
+  // computed ahead of the K loop and kept live through it, which pushed the
+  // eight-wave FC1 tile into spills.
+  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid_in));
+  const int lane = tid & 63;
+  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int wm0 = (wave / C::WAVES_N) * C::WM;
+  const int wn0 = (wave % C::WAVES_N) * C::WN;
+  const int l32 = lane & 31;
+  const int g = lane >> 5;
+  // rows this unit stores (none for a unit run only to keep a block's halves in step)
+  const int srows = store ? mrows : 0;
+  constexpr int HF = C::FN / 2;
+  if constexpr (OUT == MOE_OUT_FP32) {
+    // fp32: straight from the accumulators, one fragment at a time
+    if constexpr (EPI == 0) {
+      // fragment fh holds 32-column block 2fh, fragment fh + FN/2 block 2fh + 1
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fh = 0; fh < HF; ++fh) {
+          const int n = nt * kBN + wn0 + 2 * fh * 32 + l32;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+            float* const crow = static_cast<float*>(p.c) + (size_t)(row0 + r) * p.N;
+            if (r < srows && n < p.N) crow[n] = acc[fm][fh][q];
+            if (r < srows && n + 32 < p.N) crow[n + 32] = acc[fm][fh + HF][q];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+      const int i_base = nt * (kBN / 2) + (wave % C::WAVES_N) * (C::WN / 2);
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fh = 0; fh < HF; ++fh) {
+          const int i = i_base + fh * 32 + l32;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+            const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
+            if (r < srows && i < p.n_out) static_cast<float*>(p.c)[(size_t)(row0 + r) * p.n_out + i] = a;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+  } else {
+    // bf16 and MXFP8: the tile goes through LDS (row-major, rows padded by 16
+    // bytes) so that the global stores are whole row segments
+    constexpr bool MX = OUT == MOE_OUT_MXFP8_E4M3;
+    static_assert(!MX || EPI != 0, "MXFP8 output needs the SwiGLU epilogue");
+    constexpr int EB = MX ? 4 : 2;                   // bytes per staged element
+    constexpr int TC = EPI == 0 ? kBN : kBN / 2;    // tile columns
+    constexpr int PITCH = EB * TC + 16;
+    static_assert(BM * PITCH <= C::LDS_TOTAL, "C tile must fit in LDS");
+    stage_barrier();   // every wave is done reading the stage buffers
+    if constexpr (EPI == 0) {
+      // fragment fh holds 32-column block 2fh, fragment fh + FN/2 block 2fh + 1
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fh = 0; fh < HF; ++fh) {
+          uint8_t* col = lds + (wn0 + 2 * fh * 32 + l32) * 2;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+            // v_cvt_pk_bf16_f32 (RNE)
+            *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)acc[fm][fh][q];
+            *reinterpret_cast<__bf16*>(col + 64 + r * PITCH) = (__bf16)acc[fm][fh + HF][q];
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    } else {
+#pragma unroll
+      for (int fm = 0; fm < C::FM; ++fm)
+#pragma unroll
+        for (int fh = 0; fh < HF; ++fh) {
+          uint8_t* col = lds + ((wave % C::WAVES_N) * (C::WN / 2) + fh * 32 + l32) * EB;
+#pragma unroll
+          for (int q = 0; q < 16; ++q) {
+            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
+            const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
+            if constexpr (MX) *reinterpret_cast<float*>(col + r * PITCH) = a;
+            else *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)a;
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+    }
+    stage_barrier();
+    const int ld = EPI == 0 ? p.N : p.n_out;
+    const int col0 = nt * TC;
+    const int ncols = min(TC, ld - col0);
+    if constexpr (!MX) {
+      const bool vec = ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && (ld % 8 == 0);
+      constexpr int CPR = TC / 8;   // 16-byte chunks per tile row
+      uint16_t* const out = static_cast<uint16_t*>(p.c) + (size_t)row0 * ld + col0;
+      for (int idx = tid; idx < srows * CPR; idx += C::NT) {
+        const int r = idx / CPR, c = (idx % CPR) * 8;
+        if (c >= ncols) continue;
+        const uint4 v = *reinterpret_cast<const uint4*>(lds + r * PITCH + c * 2);
+        uint16_t* dst = out + (size_t)r * ld + c;
+        if (vec && c + 8 <= ncols) {
+          *reinterpret_cast<uint4*>(dst) = v;
+        } else {
+          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+#pragma unroll
+          for (int j = 0; j < 8; ++j)
+            if (c + j < ncols) dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+        }
+      }
+    } else {
+      // one 32-element MX block per thread and step: amax -> E8M0 exponent X ->
+      // E4M3 codes of v * 2^-X; ld is a multiple of 32 (the host checks)
+      const bool vec = (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && ld % 16 == 0;
+      constexpr int BPR = TC / 32;   // blocks per tile row
+      uint8_t* const out = static_cast<uint8_t*>(p.c) + (size_t)row0 * ld + col0;
+      uint8_t* const osc = p.c_scales + (size_t)row0 * (ld / 32) + col0 / 32;
+      for (int idx = tid; idx < srows * BPR; idx += C::NT) {
+        const int r = idx / BPR, c = (idx % BPR) * 32;
+        if (c >= ncols) continue;
+        const float4* src = reinterpret_cast<const float4*>(lds + r * PITCH + c * 4);
+        float v[32];
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+          const float4 f = src[j];
+          v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
+        }
+        float amax = 0.f;
+#pragma unroll
+        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
+        const int x = mxfp8_block_exp(amax);
+        uint32_t w[8];
+#pragma unroll
+        for (int j = 0; j < 8; ++j)
+          w[j] = e4m3x4_rne(ldexpf(v[4 * j], -x), ldexpf(v[4 * j + 1], -x),
+                            ldexpf(v[4 * j + 2], -x), ldexpf(v[4 * j + 3], -x));
+        uint8_t* dst = out + (size_t)r * ld + c;
+        if (vec) {
+          reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
+          reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
+        } else {
+#pragma unroll
+          for (int j = 0; j < 32; ++j) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+        }
+        osc[(size_t)r * (ld / 32) + c / 32] = (uint8_t)(x + 127);
+      }
+    }
+  }
+  }
+}
+
 template <int BM, bool FP8, int EPI, int OUT, bool TILED>
 __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_kernel(Params p) {
   using C = Cfg2<BM, FP8, dma_waves<BM, FP8, EPI>()>;
@@ -517,11 +1094,6 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
   const int per_xcd = (units + kXcds - 1) / kXcds;
   const int u_first = xcd * per_xcd;
   const int u_end = min(units, u_first + per_xcd);
-
-  const int K = p.K;
-  const int a_row_bytes = FP8 ? K : 2 * K;
-  const int kb = K / 32;
-  const int nst = K / C::KS;
 
   // Units of an XCD's range are handed out dynamically (blocks whose units
   // end early take more; blocks that start late take fewer).  Thread
@@ -535,569 +1107,95 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
   while (u < u_end) {
     int u_next = 0;
     if (threadIdx.x == 0) u_next = atomicAdd(&p.unit_ctr[xcd], 1);
-    // Lane-derived values are recomputed per unit from an opaque copy of the
-    // thread index.  Hoisted out of the unit loop they stay live across it and
-    // get spilled, and a spill reload in the pipeline prologue would wait for
-    // every DMA in flight.
-    int tid;
-    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave / C::WAVES_N) * C::WM;
-    const int wn0 = (wave % C::WAVES_N) * C::WN;
-    const int l32 = lane & 31;
-    const int g = lane >> 5;
-    // 32-column block of the tile that B fragment j of this wave reads.  Tile
-    // columns come in groups of 64 (32 gate rows, then their 32 up rows) for
-    // every tile class; the wave's fragments are ordered even blocks first, so
-    // that with a SwiGLU epilogue fragment fh (gate) and fh + FN/2 (up) pair
-    // up.  Without one the epilogue writes the same pairs side by side: that
-    // order is also what keeps the eight-wave FC2 tile free of spills (its
-    // identity order spilled 24-33 VGPRs of DMA offsets and LDS addresses
-    // inside the K loop).
-    auto frag_block = [](int j) { return (j % (C::FN / 2)) * 2 + j / (C::FN / 2); };
-    // fragment rows / lines start at multiples of 16, so the swizzles depend on the lane only
-    const int xa = a_swz<FP8>(l32 & 15);
-    const int xb = b_swz((l32 >> 1) & 7);
-
-    // units in groups of up to 4 row tiles x all n-tiles, row tile fastest, so
-    // that concurrent blocks of one XCD share both their A rows and their B tiles
-    constexpr int GM = 4;
-    const int grp = u / (GM * p.n_tiles);
-    const int first = grp * GM;
-    const int gsize = min(GM, count - first);
-    const int in = u - grp * GM * p.n_tiles;
-    const int ti = first + in % gsize;
-    const int nt = in / gsize;
-    const Tile tile = p.tiles[ti];
-    const int e = tile.expert;
-    const int row0 = tile.row0;
-    const int mrows = min(BM, p.offsets[e + 1] - row0);
-    const size_t w_expert = (size_t)e * p.N;
-
-    // ---- DMA sources: uniform bases, 32-bit per-lane byte offsets (stage 0) ----
-    // gathered A rows: offsets from the start of A; contiguous A rows: from the tile's first row
-    const bool gather = p.a_gather != nullptr;
-    const uint8_t* const a_base = gather ? p.a : p.a + (size_t)row0 * a_row_bytes;
-    uint32_t a_off[C::A_I];
-    {
-      int arow[C::A_I];
-#pragma unroll
-      for (int i = 0; i < C::A_I; ++i)
-        arow[i] = min((wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA, mrows - 1);
-      if (gather) {
-        // all index loads in flight together
-#pragma unroll
-        for (int i = 0; i < C::A_I; ++i) arow[i] = p.a_gather[row0 + arow[i]];
-#pragma unroll
-        for (int i = 0; i < C::A_I; ++i) arow[i] /= p.a_gather_div;
-      }
-#pragma unroll
-      for (int i = 0; i < C::A_I; ++i) {
-        const int r = (wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA;
-        const int chunk = (lane % C::SA) ^ a_swz<FP8>(r);
-        a_off[i] = (uint32_t)arow[i] * (uint32_t)a_row_bytes + chunk * 16;
-      }
-    }
-    // B: canonical weights are addressed row by row (tile column j of the
-    // stage's LDS layout <- its weight row); tiled weights already hold the
-    // stage's 16 KB in LDS order, so each instruction copies 1 KB of
-    // consecutive bytes.  b_step / bs_step: bytes from one stage (one scale
-    // group) to the next.
-    const size_t tile_id = (size_t)e * p.n_tiles + nt;
-    const uint8_t* const b_base = TILED ? p.w + tile_id * (size_t)nst * C::LDS_B : p.w + w_expert * (size_t)(K / 2);
-    const int b_step = TILED ? C::LDS_B : C::RB;
-    uint32_t b_off[C::B_I];
-#pragma unroll
-    for (int i = 0; i < C::B_I; ++i) {
-      const int line = (wave * C::B_I + i) * 8 + lane / 8;
-      const int uu = (lane & 7) ^ b_swz(line);
-      const int j = line * 2 + (uu >> 2);
-      const int wr = w_row_of<kSwiGroup>(p.layout, nt, j, p.N, p.n_out);
-      b_off[i] = TILED ? (uint32_t)((wave * C::B_I + i) * 1024 + lane * 16)
-                           : (uint32_t)wr * (uint32_t)(K / 2) + (uu & 3) * 16;
-    }
-    // scale loads: with four waves every wave loads 64 rows of A scales (if
-    // below BM) and 64 of B scales; with eight, waves 0-3 load A, 4-7 load B
-    const bool a_sw = C::NW == 8 ? wave < 4 : true;
-    const bool b_sw = C::NW == 8 ? wave >= 4 : true;
-    const int sw = (C::NW == 8 && wave >= 4) ? wave - 4 : wave;
-    const int srow = sw * 64 + lane;   // scale row this lane loads (A: if < BM)
-    const uint8_t* const as_base = gather ? p.a_scales : p.a_scales + (size_t)row0 * kb;
-    uint32_t as_off = 0;
-    if (FP8 && a_sw && srow < BM) {
-      const int r = min(srow, mrows - 1);
-      as_off = (uint32_t)(gather ? p.a_gather[row0 + r] / p.a_gather_div : r) * (uint32_t)kb;
-    }
-    const uint8_t* const bs_base =
-        TILED ? p.w_scales + tile_id * (size_t)(K / 512) * 4096 : p.w_scales + w_expert * (size_t)kb;
-    const int bs_step = TILED ? 4096 : 16;
-    const uint32_t bs_off = TILED ? (uint32_t)(sw * 1024 + lane * 16)
-                                      : (uint32_t)w_row_of<kSwiGroup>(p.layout, nt, srow, p.N, p.n_out) * (uint32_t)kb;
-    uint8_t* const sg = lds + C::NST * C::LDS_STAGE;   // two scale groups
-
-    const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
-    const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
-    const __amdgpu_buffer_rsrc_t ras = make_rsrc(as_base);
-    const __amdgpu_buffer_rsrc_t rbs = make_rsrc(bs_base);
-    auto issue = [&](int s) {
-      uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
-#pragma unroll
-      for (int i = 0; i < C::A_I; ++i) dma16(ra, a_off[i], s * C::RA, base + (wave * C::A_I + i) * 1024);
-#pragma unroll
-      for (int i = 0; i < C::B_I; ++i)
-        dma16(rb, b_off[i], s * b_step, base + C::LDS_A + (wave * C::B_I + i) * 1024);
-    };
-    // DMA instruction j of stage s (j < A_I: A, then B), for interleaving with products
-    auto issue_one = [&](int s, int j) {
-      uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
-      if (j < C::A_I) dma16(ra, a_off[j], s * C::RA, base + (wave * C::A_I + j) * 1024);
-      else dma16(rb, b_off[j - C::A_I], s * b_step, base + C::LDS_A + (wave * C::B_I + j - C::A_I) * 1024);
-    };
-    // scale group j (stages 4j..4j+3): 16 bytes of every A and B row
-    auto issue_scales = [&](int j) {
-      uint8_t* base = sg + (j & 1) * C::LDS_SG;
-      // (a 32-row tile has 512 bytes of A scales per group: lanes 32-63 stay idle)
-      if (FP8 && a_sw && sw * 64 < BM && (BM >= 64 || lane < BM)) dma16(ras, as_off, 16 * j, base + sw * 1024);
-      if (b_sw) dma16(rbs, bs_off, bs_step * j, base + C::SG_A + sw * 1024);
-    };
-
-    v16f acc[C::FM][C::FN];
-#pragma unroll
-    for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-      for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
-
-    if constexpr (FP8) {
-      uint32_t sa[C::FM], sb[C::FN], na[C::FM], nb[C::FN];
-      v8i a0[C::FM], a1[C::FM];
-      v4i b0[C::FN], b1[C::FN];
-      // LDS base of stage s, made opaque to the compiler: otherwise every
-      // fragment address becomes an induction variable of its own
-      auto stage_lds = [&](int s) {
-        return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
-      };
-      // read j of one k-half: j < FN: B fragment j; then the A fragments' low and high halves
-      // (A: K [kk*64 + 16g, +16) and [kk*64 + 32 + 16g, +16) = chunks 4kk+g and 4kk+2+g)
-      auto read_frag = [&](int s, int kk, int j, v8i (&af)[C::FM], v4i (&bq)[C::FN]) {
-        const uint8_t* la = stage_lds(s);
-        if (j < C::FN) {
-          const int n = wn0 + frag_block(j) * 32 + l32;
-          const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xb;
-          bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
-        } else {
-          const int fm = (j - C::FN) >> 1, hi = (j - C::FN) & 1;
-          const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
-          const v4i v = *reinterpret_cast<const v4i*>(row + (((4 * kk + 2 * hi + g) ^ xa) << 4));
-          if (hi) {
-            af[fm][4] = v[0]; af[fm][5] = v[1]; af[fm][6] = v[2]; af[fm][7] = v[3];
-          } else {
-            af[fm][0] = v[0]; af[fm][1] = v[1]; af[fm][2] = v[2]; af[fm][3] = v[3];
-          }
-        }
-      };
-      // scale word j of stage s: four E8M0 bytes (the stage's blocks) of an A row or B column
-      auto read_scale = [&](int s, int j, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
-        const uint8_t* lsg = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4);
-        if (j < C::FM) ta[j] = *reinterpret_cast<const uint32_t*>(lsg + (wm0 + j * 32 + l32) * 16);
-        else tb[j - C::FM] = *reinterpret_cast<const uint32_t*>(lsg + C::SG_A + (wn0 + frag_block(j - C::FM) * 32 + l32) * 16);
-      };
-      // product i of one k-half, B-fragment major.  ta/tb hold this lane's scale
-      // bytes in the order the op_sel field reads them: byte kk = block 2kk + g.
-      auto mma = [&](int kk, int i, const v8i (&af)[C::FM], const v4i (&bq)[C::FN], const uint32_t (&ta)[C::FM],
-                     const uint32_t (&tb)[C::FN]) {
-        const int fn = i / C::FM, fm = i % C::FM;
-        const v8i bf = v8i{bq[fn][0], bq[fn][1], bq[fn][2], bq[fn][3], 0, 0, 0, 0};
-        if (kk == 0)
-          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0 /*A: fp8 e4m3*/,
-                                                                        4 /*B: fp4 e2m1*/, 0, ta[fm], 0, tb[fn]);
-        else
-          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0, 4, 1, ta[fm],
-                                                                        1, tb[fn]);
-      };
-      // a stage's four scale bytes (blocks 0..3) -> this lane's two, in op_sel order
-      const uint32_t scale_sel = g ? 0x0c0c0301u : 0x0c0c0200u;
-      auto order_scales = [&](uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
-#pragma unroll
-        for (int j = 0; j < C::FM; ++j) ta[j] = __builtin_amdgcn_perm(0u, ta[j], scale_sel);
-#pragma unroll
-        for (int j = 0; j < C::FN; ++j) tb[j] = __builtin_amdgcn_perm(0u, tb[j], scale_sel);
-      };
-      constexpr int MF = C::FM * C::FN;
-      constexpr int NR = 2 * C::FM + C::FN;   // fragment reads of one k-half
-      constexpr int NS = C::FM + C::FN;       // scale reads of one stage
-      // reads issued after each product: at least two (front-loaded), more for small tiles
-      constexpr int R1 = (NR + MF - 1) / MF > 2 ? (NR + MF - 1) / MF : 2;
-      constexpr int R2 = (NR + NS + MF - 1) / MF > 2 ? (NR + NS + MF - 1) / MF : 2;
-      constexpr int D2 = (C::LOADS + MF - 1) / MF;   // refill DMA instructions per product
-      // One stage.  ISSUE: refill the freed buffer with stage s+3 during the second
-      // half (SCALES: and the next scale group); WAIT: vmcnt allowance at the
-      // mid-stage barrier, -1 for the last stage (no barrier, no next-stage
-      // reads).  All three are compile-time constants so that the loop body has
-      // no branch the compiler could sink the first half's products past.  Every
-      // group of one product and its reads / DMA is fenced with sched_barrier to
-      // keep the interleave.
-      auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN],
-                      uint32_t (&tna)[C::FM], uint32_t (&tnb)[C::FN]) {
-        constexpr bool kIssue = decltype(ISSUE)::value;
-        constexpr bool kScales = decltype(SCALES)::value;
-        constexpr int kWait = decltype(WAIT)::value;
-        order_scales(ta, tb);
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          mma(0, i, a0, b0, ta, tb);
-          __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-          for (int r = R1 * i; r < R1 * i + R1; ++r)
-            if (r < NR) read_frag(s, 1, r, a1, b1);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-        // the first half's products stay ahead of the barrier
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
-        if constexpr (kWait >= 0) {
-          // stage s fully read by this wave; stage s+1 landed for this wave's loads
-          wait_lgkm0();
-          wait_vm<kWait>();
-          stage_barrier();
-        }
-        __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          mma(1, i, a1, b1, ta, tb);
-          __builtin_amdgcn_sched_barrier(0);
-          if constexpr (kWait >= 0) {
-#pragma unroll
-            for (int r = R2 * i; r < R2 * i + R2; ++r) {
-              if (r < NS) read_scale(s + 1, r, tna, tnb);
-              else if (r < NS + NR) read_frag(s + 1, 0, r - NS, a0, b0);
-            }
-          }
-          // the refill of the freed buffer (stage s+3), spread over the products
-          if constexpr (kIssue) {
-#pragma unroll
-            for (int j = D2 * i; j < D2 * i + D2; ++j) {
-              if (j < C::LOADS) issue_one(s + 3, j);
-              if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
-            }
-          }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      using T = std::integral_constant<bool, true>;
-      using F = std::integral_constant<bool, false>;
-      using WL = std::integral_constant<int, C::LOADS>;   // stage s+2 may still be in flight
-      issue_scales(0);
-      issue(0);
-      issue(1);
-      issue(2);
-      wait_vm<2 * C::LOADS>();
-      stage_barrier();
-#pragma unroll
-      for (int r = 0; r < NS; ++r) read_scale(0, r, sa, sb);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) read_frag(0, 0, r, a0, b0);
-      // the stage count is a multiple of four (K % 512 == 0): groups of four stages,
-      // the last group with its tail conditions resolved at compile time
-      int s = 0;
-      for (; s + 4 < nst; s += 4) {
-        step(s, T{}, F{}, WL{}, sa, sb, na, nb);
-        step(s + 1, T{}, T{}, WL{}, na, nb, sa, sb);
-        step(s + 2, T{}, F{}, WL{}, sa, sb, na, nb);
-        step(s + 3, T{}, F{}, WL{}, na, nb, sa, sb);
-      }
-      step(s, T{}, F{}, WL{}, sa, sb, na, nb);
-      step(s + 1, F{}, F{}, WL{}, na, nb, sa, sb);
-      step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sa, sb, na, nb);
-      step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, na, nb, sa, sb);
-    } else {
-      // bf16 A: the same pipeline as the FP8 path, with k-halves of 64 elements
-      // (block h of each lane half), the weights expanded to bf16 in registers
-      // (one conversion unit = 8 weights of one column, 4 instructions) spread
-      // over the products of the preceding 16-element step
-      uint32_t sb[C::FN], nb[C::FN];
-      v4i bqc[C::FN], bqn[C::FN];            // raw FP4 B of the current / next k-half
-      v8bf afc[4][C::FM], afn[4][C::FM];     // A of the current / next k-half, per 16-element step
-      v8bf bw[C::FN][4];                     // B of the current k-half, expanded
-      auto stage_lds = [&](int s) {
-        return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
-      };
-      // read j of k-half h: j < FN: raw B of column fragment j; then A (step, fm)
-      auto read_frag = [&](int s, int h, int j, v4i (&bq)[C::FN], v8bf (&af)[4][C::FM]) {
-        const uint8_t* la = stage_lds(s);
-        if (j < C::FN) {
-          const int n = wn0 + frag_block(j) * 32 + l32;
-          const int uu = ((n & 1) * 4 + 2 * h + g) ^ xb;
-          bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
-        } else {
-          const int s4 = (j - C::FN) / C::FM, fm = (j - C::FN) % C::FM;
-          const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
-          // bytes 128h + 64g + 16*s4 of the 256-byte stage row: slot 8h + 4g + s4
-          af[s4][fm] = *reinterpret_cast<const v8bf*>(row + (((8 * h + 4 * g + s4) ^ xa) << 4));
-        }
-      };
-      auto read_scale = [&](int s, int j, uint32_t (&tb)[C::FN]) {
-        const uint8_t* lsb = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4) + C::SG_A;
-        tb[j] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + frag_block(j) * 32 + l32) * 16);
-      };
-      // conversion unit (fn, d): the 8 weights of bw[fn][d] (E2M1 x block scale -> bf16, exact)
-      auto expand = [&](int h, int fn, int d, const v4i (&bq)[C::FN], const uint32_t (&tb)[C::FN]) {
-        const float sc = e8m0_to_f32((tb[fn] >> (8 * (2 * h + g))) & 0xff);
-        const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 0);
-        const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 1);
-        const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 2);
-        const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 3);
-        bw[fn][d] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      };
-      constexpr int MG = C::FN * C::FM;      // products of one 16-element step
-      constexpr int MF = 4 * MG;             // products of one k-half
-      constexpr int NR = C::FN + 4 * C::FM;  // reads of one k-half
-      constexpr int NS = C::FN;              // scale reads of one stage
-      constexpr int R1 = (NR + MF - 1) / MF > 1 ? (NR + MF - 1) / MF : 1;
-      constexpr int R2 = (NR + NS + MF - 1) / MF > 1 ? (NR + NS + MF - 1) / MF : 1;
-      constexpr int D2 = (C::LOADS + MF - 1) / MF;
-      // the products of k-half h from af/bq, with the expansion of step t+1's
-      // weights after the MFMAs of step t (unit fn after the step's product fn*FM),
-      // and EXTRA(i) (reads / DMA) after product i
-      auto half = [&](int h, const v4i (&bq)[C::FN], const v8bf (&af)[4][C::FM], const uint32_t (&tb)[C::FN],
-                      auto&& extra) {
-#pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) expand(h, fn, 0, bq, tb);
-#pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          const int s4 = i / MG, fn = (i % MG) / C::FM, fm = i % C::FM;
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s4][fm], bw[fn][s4], acc[fm][fn], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (s4 < 3 && fm == 0) expand(h, fn, s4 + 1, bq, tb);
-          extra(i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&tb)[C::FN], uint32_t (&tnb)[C::FN]) {
-        constexpr bool kIssue = decltype(ISSUE)::value;
-        constexpr bool kScales = decltype(SCALES)::value;
-        constexpr int kWait = decltype(WAIT)::value;
-        half(0, bqc, afc, tb, [&](int i) {
-#pragma unroll
-          for (int r = R1 * i; r < R1 * i + R1; ++r)
-            if (r < NR) read_frag(s, 1, r, bqn, afn);
-        });
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
-        if constexpr (kWait >= 0) {
-          wait_lgkm0();
-          wait_vm<kWait>();
-          stage_barrier();
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        half(1, bqn, afn, tb, [&](int i) {
-          if constexpr (kWait >= 0) {
-#pragma unroll
-            for (int r = R2 * i; r < R2 * i + R2; ++r) {
-              if (r < NS) read_scale(s + 1, r, tnb);
-              else if (r < NS + NR) read_frag(s + 1, 0, r - NS, bqc, afc);
-            }
-          }
-          if constexpr (kIssue) {
-#pragma unroll
-            for (int j = D2 * i; j < D2 * i + D2; ++j) {
-              if (j < C::LOADS) issue_one(s + 3, j);
-              if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
-            }
-          }
-        });
-      };
-      using T = std::integral_constant<bool, true>;
-      using F = std::integral_constant<bool, false>;
-      using WL = std::integral_constant<int, C::LOADS>;
-      issue_scales(0);
-      issue(0);
-      issue(1);
-      issue(2);
-      wait_vm<2 * C::LOADS>();
-      stage_barrier();
-#pragma unroll
-      for (int r = 0; r < NS; ++r) read_scale(0, r, sb);
-#pragma unroll
-      for (int r = 0; r < NR; ++r) read_frag(0, 0, r, bqc, afc);
-      int s = 0;
-      for (; s + 4 < nst; s += 4) {
-        step(s, T{}, F{}, WL{}, sb, nb);
-        step(s + 1, T{}, T{}, WL{}, nb, sb);
-        step(s + 2, T{}, F{}, WL{}, sb, nb);
-        step(s + 3, T{}, F{}, WL{}, nb, sb);
-      }
-      step(s, T{}, F{}, WL{}, sb, nb);
-      step(s + 1, F{}, F{}, WL{}, nb, sb);
-      step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sb, nb);
-      step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, nb, sb);
-    }
-
-    // ---- epilogue: registers -> C in permuted row order ----
-    // gate/up pairing of the SwiGLU layouts: fragment fh holds the gate columns
-    // of 32-column block 2fh, fragment fh + FN/2 the matching up columns of
-    // block 2fh + 1 (see frag_block)
-    {
-    // The epilogue's lane-derived values come from a fresh opaque copy of the
-    // thread index: derived from the one above, its store addresses were
-    // computed ahead of the K loop and kept live through it, which pushed the
-    // eight-wave FC1 tile into spills.
-    asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"((int)threadIdx.x));
-    const int lane = tid & 63;
-    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-    const int wm0 = (wave / C::WAVES_N) * C::WM;
-    const int wn0 = (wave % C::WAVES_N) * C::WN;
-    const int l32 = lane & 31;
-    const int g = lane >> 5;
-    constexpr int HF = C::FN / 2;
-    if constexpr (OUT == MOE_OUT_FP32) {
-      // fp32: straight from the accumulators, one fragment at a time
-      if constexpr (EPI == 0) {
-        // fragment fh holds 32-column block 2fh, fragment fh + FN/2 block 2fh + 1
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-          for (int fh = 0; fh < HF; ++fh) {
-            const int n = nt * kBN + wn0 + 2 * fh * 32 + l32;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              float* const crow = static_cast<float*>(p.c) + (size_t)(row0 + r) * p.N;
-              if (r < mrows && n < p.N) crow[n] = acc[fm][fh][q];
-              if (r < mrows && n + 32 < p.N) crow[n + 32] = acc[fm][fh + HF][q];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      } else {
-        const int i_base = nt * (kBN / 2) + (wave % C::WAVES_N) * (C::WN / 2);
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-          for (int fh = 0; fh < HF; ++fh) {
-            const int i = i_base + fh * 32 + l32;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
-              if (r < mrows && i < p.n_out) static_cast<float*>(p.c)[(size_t)(row0 + r) * p.n_out + i] = a;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      }
-    } else {
-      // bf16 and MXFP8: the tile goes through LDS (row-major, rows padded by 16
-      // bytes) so that the global stores are whole row segments
-      constexpr bool MX = OUT == MOE_OUT_MXFP8_E4M3;
-      static_assert(!MX || EPI != 0, "MXFP8 output needs the SwiGLU epilogue");
-      constexpr int EB = MX ? 4 : 2;                   // bytes per staged element
-      constexpr int TC = EPI == 0 ? kBN : kBN / 2;    // tile columns
-      constexpr int PITCH = EB * TC + 16;
-      static_assert(BM * PITCH <= C::LDS_TOTAL, "C tile must fit in LDS");
-      stage_barrier();   // every wave is done reading the stage buffers
-      if constexpr (EPI == 0) {
-        // fragment fh holds 32-column block 2fh, fragment fh + FN/2 block 2fh + 1
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-          for (int fh = 0; fh < HF; ++fh) {
-            uint8_t* col = lds + (wn0 + 2 * fh * 32 + l32) * 2;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              // v_cvt_pk_bf16_f32 (RNE)
-              *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)acc[fm][fh][q];
-              *reinterpret_cast<__bf16*>(col + 64 + r * PITCH) = (__bf16)acc[fm][fh + HF][q];
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      } else {
-#pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-          for (int fh = 0; fh < HF; ++fh) {
-            uint8_t* col = lds + ((wave % C::WAVES_N) * (C::WN / 2) + fh * 32 + l32) * EB;
-#pragma unroll
-            for (int q = 0; q < 16; ++q) {
-              const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-              const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
-              if constexpr (MX) *reinterpret_cast<float*>(col + r * PITCH) = a;
-              else *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)a;
-            }
-            __builtin_amdgcn_sched_barrier(0);
-          }
-      }
-      stage_barrier();
-      const int ld = EPI == 0 ? p.N : p.n_out;
-      const int col0 = nt * TC;
-      const int ncols = min(TC, ld - col0);
-      if constexpr (!MX) {
-        const bool vec = ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && (ld % 8 == 0);
-        constexpr int CPR = TC / 8;   // 16-byte chunks per tile row
-        uint16_t* const out = static_cast<uint16_t*>(p.c) + (size_t)row0 * ld + col0;
-        for (int idx = tid; idx < mrows * CPR; idx += C::NT) {
-          const int r = idx / CPR, c = (idx % CPR) * 8;
-          if (c >= ncols) continue;
-          const uint4 v = *reinterpret_cast<const uint4*>(lds + r * PITCH + c * 2);
-          uint16_t* dst = out + (size_t)r * ld + c;
-          if (vec && c + 8 <= ncols) {
-            *reinterpret_cast<uint4*>(dst) = v;
-          } else {
-            const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-            for (int j = 0; j < 8; ++j)
-              if (c + j < ncols) dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
-          }
-        }
-      } else {
-        // one 32-element MX block per thread and step: amax -> E8M0 exponent X ->
-        // E4M3 codes of v * 2^-X; ld is a multiple of 32 (the host checks)
-        const bool vec = (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && ld % 16 == 0;
-        constexpr int BPR = TC / 32;   // blocks per tile row
-        uint8_t* const out = static_cast<uint8_t*>(p.c) + (size_t)row0 * ld + col0;
-        uint8_t* const osc = p.c_scales + (size_t)row0 * (ld / 32) + col0 / 32;
-        for (int idx = tid; idx < mrows * BPR; idx += C::NT) {
-          const int r = idx / BPR, c = (idx % BPR) * 32;
-          if (c >= ncols) continue;
-          const float4* src = reinterpret_cast<const float4*>(lds + r * PITCH + c * 4);
-          float v[32];
-#pragma unroll
-          for (int j = 0; j < 8; ++j) {
-            const float4 f = src[j];
-            v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
-          }
-          float amax = 0.f;
-#pragma unroll
-          for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-          const int x = mxfp8_block_exp(amax);
-          uint32_t w[8];
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            w[j] = e4m3x4_rne(ldexpf(v[4 * j], -x), ldexpf(v[4 * j + 1], -x),
-                              ldexpf(v[4 * j + 2], -x), ldexpf(v[4 * j + 3], -x));
-          uint8_t* dst = out + (size_t)r * ld + c;
-          if (vec) {
-            reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-            reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-          } else {
-#pragma unroll
-            for (int j = 0; j < 32; ++j) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
-          }
-          osc[(size_t)r * (ld / 32) + c / 32] = (uint8_t)(x + 127);
-        }
-      }
-    }
-    }
+    run_unit<BM, FP8, EPI, OUT, TILED, C::NW>(p, u, count, threadIdx.x, lds, true);
     // every wave is done with LDS before the next unit refills it
     stage_barrier();
     if (threadIdx.x == 0) *unit_slot = u_next;
     stage_barrier();
     u = u_first + *unit_slot;
+  }
+}
+
+// ---- every row-tile class of a call in one launch ------------------------
+//
+// The full 256-row tiles are bound by the matrix cores; the <= 32-row tiles
+// (the remainders of experts with few rows: the tail of a skewed routing)
+// only stream their experts' weights, and the 64- and 128-row tiles sit in
+// between.  Run one class after another, the weight stream runs with the
+// matrix cores idle, and a <= 32-row block streams at most about 35 GB/s
+// however few blocks run beside it (latency-bound per block), so that stream
+// needs many CUs at once.  Here every CU runs one block of eight waves that
+// works through the classes' unit queues in turn: kSmallCus blocks per XCD
+// take the <= 32-row units first (two at a time: waves 0-3 and 4-7 each run
+// one unit in their own half of the LDS), then the 64-, 128- and 256-row
+// ones; the other blocks take them in the opposite order.  The weight stream
+// of the small units then runs under the matrix-core work of the other CUs,
+// and every block stays busy until the last queue is empty.  Both halves of
+// a block run the same barriers: a half without a unit of its own runs its
+// partner's unit without storing it.  Units are drawn per XCD from the
+// planner's lists as the single-class launches draw them (one unit ahead), so
+// every output row is written once, by the same per-unit code.
+constexpr int kSmallHalfLds = 81920;   // LDS of one half running a <= 32-row unit
+constexpr int kSmallCus = 4;           // blocks per XCD that start on the <= 32-row units
+
+template <bool FP8, int EPI, int OUT>
+__global__ __launch_bounds__(512) void gemm_mixed_kernel(Params p, int small_cus) {
+  using CF = Cfg2<256, FP8, 8>;
+  using CS = Cfg2<32, FP8, 4>;
+  static_assert(CS::LDS_TOTAL <= kSmallHalfLds, "a <= 32-row unit fits half the LDS");
+  constexpr int kSlots = CF::NST * CF::LDS_STAGE + CF::LDS_SG;   // idle between units
+  static_assert(kSmallHalfLds + CS::LDS_TOTAL <= kSlots && Cfg2<128, FP8, 8>::LDS_TOTAL <= kSlots,
+                "the draw slots lie beyond every unit's LDS");
+  __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::LDS_TOTAL];
+  int* const slot = reinterpret_cast<int*>(lds + kSlots);   // this block's next draw, per half
+
+  const int xcd = blockIdx.x % kXcds;
+  const bool small_first = blockIdx.x / kXcds < small_cus;
+  const int half = threadIdx.x >> 8;
+  const Tile* const lists = p.tiles;
+  const int32_t* const counts = p.tile_count;
+  int32_t* const ctr = p.unit_ctr;
+
+  int ph = 0;          // position in this block's queue order
+  bool have = false;   // the slots already hold the next draws from the current queue
+  while (ph < kClasses) {
+    const int c = small_first ? ph : kClasses - 1 - ph;   // row-tile class of the current queue
+    const bool dual = c == 0;
+    const int cnt = counts[c];
+    const int units = cnt * p.n_tiles;
+    const int per_xcd = (units + kXcds - 1) / kXcds;
+    const int u0 = xcd * per_xcd, u1 = min(units, u0 + per_xcd);
+    int32_t* const uc = ctr + c * kXcds + xcd;
+    // the threads that draw: thread 0 (a single unit) or the first of each half
+    const bool drawer = dual ? (threadIdx.x & 255) == 0 : threadIdx.x == 0;
+    if (!have && drawer) slot[half] = atomicAdd(uc, 1);
+    stage_barrier();
+    const int a = u0 + slot[0], b = u0 + slot[1];
+    stage_barrier();   // both slots read before either is written again
+    const bool va = a < u1, vb = dual && b < u1;
+    if (!va && !vb) {
+      ++ph;
+      have = false;
+      continue;
+    }
+    int nxt = 0;
+    if (drawer) nxt = atomicAdd(uc, 1);   // one unit ahead
+    Params q = p;
+    q.tiles = lists + c * p.tile_cap;
+    if (c == 3) {
+      run_unit<256, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true);
+    } else if (c == 2) {
+      run_unit<128, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true);
+    } else if (c == 1) {
+      run_unit<64, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true);
+    } else {
+      const bool mine = half ? vb : va;
+      const int u = (half ? vb : !va) ? b : a;   // a half without a unit runs its partner's
+      run_unit<32, FP8, EPI, OUT, true, 4>(q, u, cnt, threadIdx.x & 255, lds + half * kSmallHalfLds, mine);
+    }
+    stage_barrier();   // every wave is done with the LDS
+    if (drawer) slot[half] = nxt;
+    have = true;
   }
 }
 
@@ -1315,6 +1413,20 @@ moe_status launch_all(Params p, const Tile* lists, int cap, const int32_t* count
     p.tile_count = counts + c;
     p.unit_ctr = ctr + c * kXcds;
   };
+  if constexpr (FP8 && PATH == 2) {
+    // every class in one launch when the full 256-row class can have tiles
+    if (reserve == 0 && max_rows >= kClassMinRows[3]) {
+      Params q = p;
+      q.tiles = lists;
+      q.tile_cap = cap;
+      q.tile_count = counts;
+      q.unit_ctr = ctr;
+      hipLaunchKernelGGL((gemm_mixed_kernel<FP8, EPI, OUT>), dim3(num_cus() / kXcds * kXcds), dim3(512), 0, s,
+                         q, kSmallCus);
+      MXMOE_HIP(hipGetLastError());
+      return MOE_OK;
+    }
+  }
   at(0); MXMOE_TRY((launch_class<32, FP8, EPI, OUT, PATH>(p, s, reserve)));
   if (max_rows < kClassMinRows[1]) return MOE_OK;
   at(1); MXMOE_TRY((launch_class<64, FP8, EPI, OUT, PATH>(p, s, reserve)));
