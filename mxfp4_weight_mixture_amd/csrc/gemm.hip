@@ -393,18 +393,20 @@ __global__ __launch_bounds__(kThreads) void gemm_kernel(Params p) {
 // ones, with no padding.
 
 // Waves per block.  The full FP8 tiles run eight (two per SIMD, each wave a
-// 64x128 slice): measured faster than four 128x128 waves.  The full bf16
-// tile (128 rows) runs eight waves of 64x64: with four, one wave per SIMD
-// both expands the FP4 weights to bf16 on the vector ALU and feeds the
-// matrix core.
+// 64x128 slice): measured faster than four 128x128 waves.  The bf16 tiles
+// run four: their waves expand their FP4 weights to bf16 on the vector ALU
+// (v_cvt_scalef32_pk_bf16_fp4, two weights an instruction), and that
+// expansion, not the matrix core, bounds them; a 128-row tile therefore
+// gives each wave all 128 rows (128x64 slices), so that every expanded
+// weight feeds four 32-row products.
 template <int BM, bool FP8, int EPI>
-constexpr int dma_waves() { return ((BM == 256 && FP8) || (BM == 128 && !FP8)) ? 8 : 4; }
+constexpr int dma_waves() { return (BM == 256 && FP8) ? 8 : 4; }
 
 template <int BM, bool FP8, int NWAVES = 4>
 struct Cfg2 {
   static constexpr int NW = NWAVES;
   static constexpr int NT = NW * 64;
-  static constexpr int WAVES_M = NW == 8 ? (BM == 256 ? 4 : 2) : (BM >= 128 ? 2 : 1);
+  static constexpr int WAVES_M = NW == 8 ? (BM == 256 ? 4 : 2) : (BM >= 128 && FP8 ? 2 : 1);
   static constexpr int WAVES_N = NW / WAVES_M;
   static constexpr int WM = BM / WAVES_M;
   static constexpr int WN = kBN / WAVES_N;
