@@ -236,24 +236,63 @@ def test_gemm_small_tiles_long_k_against_oracle(fp8, layout, K):
 @pytest.mark.parametrize("fp8", [False, True])
 @pytest.mark.parametrize("layout,out", [("none", "fp32"), ("none", "bf16"), ("split", "bf16")])
 def test_gemm_32_and_64_row_classes_agree_bitwise(fp8, layout, out, K):
-    """A 32-row expert (32-row tile class) and the first 32 rows of the same
-    expert given 33 rows (64-row class) accumulate every output in the same K
-    order, so they must agree bitwise."""
+    """Two experts with the same weights in one call: expert 0 gets 32 rows
+    (32-row tile class), expert 1 the same 32 rows plus one (64-row class).
+    Both tiles accumulate every output in the same K order, so expert 0's rows
+    equal expert 1's first 32 bitwise."""
     g = np.random.default_rng(3 * K + fp8)
     N = 512
     x = torch.from_numpy(g.standard_normal((33, K)).astype(np.float32)).to(torch.bfloat16)
     wp, ws = _rand_w(1, N, K, seed=K + 1)
+    wp, ws = np.concatenate([wp, wp]), np.concatenate([ws, ws])
+    rows = torch.cat([torch.arange(32), torch.arange(33)]).to(torch.int32)
+    if fp8:
+        codes, scales = gen.quantize_mxfp8(x.float())
+        a, a_sc = codes[rows].to(DEV), scales[rows].to(DEV)
+    else:
+        a, a_sc = x[rows].to(DEV), None
+    w = (torch.from_numpy(wp).to(DEV), torch.from_numpy(ws).to(DEV))
+    c = mx.grouped_gemm(a, *w, torch.from_numpy(_offsets([32, 33])).to(DEV), a_scales=a_sc,
+                        epilogue=layout, out_dtype=out)
+    assert torch.equal(c[:32], c[32:64])
+
+
+@pytest.mark.parametrize("fp8", [False, True])
+@pytest.mark.parametrize("layout,out", [("none", "fp32"), ("none", "bf16"), ("split", "bf16"),
+                                        ("interleaved", "mxfp8")])
+def test_gemm_decode_shaped_call_matches_oracle_and_repeats_bitwise(fp8, layout, out):
+    """A call of 32 rows in all (the decode shape: only the 32-row tile class
+    runs) over a long K meets the oracle's bound (the MXFP8 output checked
+    through its decoded values), and repeated calls are bitwise identical."""
+    if out == "mxfp8" and not fp8:
+        fp8 = True
+    g = np.random.default_rng(41 + fp8)
+    K, N, counts = 4096, 512, [1, 0, 24, 7]
+    off = _offsets(counts)
+    rows = sum(counts)
+    x = torch.from_numpy(g.standard_normal((rows, K)).astype(np.float32)).to(torch.bfloat16)
+    wp, ws = _rand_w(len(counts), N, K, seed=77)
     if fp8:
         codes, scales = gen.quantize_mxfp8(x.float())
         a, a_sc = codes.to(DEV), scales.to(DEV)
+        a64 = omx.dequant_mxfp8(codes.numpy(), scales.numpy())
     else:
         a, a_sc = x.to(DEV), None
-    w = (torch.from_numpy(wp).to(DEV), torch.from_numpy(ws).to(DEV))
-    c32 = mx.grouped_gemm(a[:32], *w, torch.from_numpy(_offsets([32])).to(DEV),
-                          a_scales=a_sc[:32] if fp8 else None, epilogue=layout, out_dtype=out)
-    c33 = mx.grouped_gemm(a, *w, torch.from_numpy(_offsets([33])).to(DEV), a_scales=a_sc,
-                          epilogue=layout, out_dtype=out)
-    assert torch.equal(c32, c33[:32])
+        a64 = omx.bf16_value(x.view(torch.int16).numpy())
+    args = dict(a_scales=a_sc, epilogue=layout, out_dtype=out)
+    w = (torch.from_numpy(wp).to(DEV), torch.from_numpy(ws).to(DEV), torch.from_numpy(off).to(DEV))
+    c = mx.grouped_gemm(a, *w, **args)
+    again = mx.grouped_gemm(a, *w, **args)
+    torch.cuda.synchronize()
+    if out == "mxfp8":
+        assert torch.equal(c[0], again[0]) and torch.equal(c[1], again[1])
+        got = omx.dequant_mxfp8(c[0].cpu().numpy(), c[1].cpu().numpy())
+    else:
+        assert torch.equal(c, again)
+        got = c.float().cpu().numpy()
+    want = _gemm_oracle(a64, np.arange(rows, dtype=np.int32), 1, wp, ws, off, layout)
+    tol = {"fp32": 1e-4 if fp8 else 1e-5, "bf16": 1e-2, "mxfp8": 5e-2}[out]
+    assert rel_err(got, want) < tol
 
 
 @pytest.mark.parametrize("fp8", [False, True])
