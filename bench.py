@@ -609,6 +609,56 @@ def bench_graph(shape, w, x, xs, logits, inter, args, w_format="canonical"):
             "note": "back-to-back steps on one stream, no per-step sync"}
 
 
+# NUMA placement of the pinned weight blobs (Linux syscalls on x86-64; the
+# pages' node is read back, so the record says where they really are)
+_SYS_SET_MEMPOLICY, _SYS_GET_MEMPOLICY = 238, 239
+_MPOL_DEFAULT, _MPOL_PREFERRED = 0, 1
+_MPOL_F_NODE, _MPOL_F_ADDR = 1, 2
+
+
+def gpu_numa_node():
+    """NUMA node of GPU 0 from sysfs (its PCI function), or -1 when the host does not say."""
+    try:
+        pr = torch.cuda.get_device_properties(0)
+        bdf = f"{pr.pci_domain_id:04x}:{pr.pci_bus_id:02x}:{pr.pci_device_id:02x}.0"
+        return int(open(f"/sys/bus/pci/devices/{bdf}/numa_node").read())
+    except Exception:
+        return -1
+
+
+def _libc():
+    import ctypes
+    return ctypes.CDLL(None, use_errno=True)
+
+
+def prefer_numa_node(node):
+    """Make this thread's new pages come from `node` (MPOL_PREFERRED); node < 0 restores the default.
+    Returns True when the policy was set.  A pinned allocation made meanwhile is placed there (the
+    lesson of ktransformers issue #2172, second comment: weight pools bound to the wrong node)."""
+    import ctypes
+    libc = _libc()
+    if node < 0:
+        return libc.syscall(_SYS_SET_MEMPOLICY, _MPOL_DEFAULT, None, ctypes.c_ulong(0)) == 0
+    mask = (ctypes.c_ulong * 16)()
+    mask[node // 64] = 1 << (node % 64)
+    return libc.syscall(_SYS_SET_MEMPOLICY, _MPOL_PREFERRED, mask, ctypes.c_ulong(16 * 64)) == 0
+
+
+def page_numa_nodes(t, samples=16):
+    """NUMA nodes holding `samples` evenly spaced pages of host tensor t (-1 where unknown)."""
+    import ctypes
+    libc = _libc()
+    out = []
+    base, n = t.data_ptr(), t.numel() * t.element_size()
+    for i in range(samples):
+        node = ctypes.c_int(-1)
+        addr = ctypes.c_void_p(base + (n - 1) * i // max(1, samples - 1))
+        rc = libc.syscall(_SYS_GET_MEMPOLICY, ctypes.byref(node), None, ctypes.c_ulong(0), addr,
+                          ctypes.c_ulong(_MPOL_F_NODE | _MPOL_F_ADDR))
+        out.append(node.value if rc == 0 else -1)
+    return out
+
+
 def bench_streamed(args):
     shape = gen.preset("streamed")
     if args.tokens:
@@ -624,6 +674,11 @@ def bench_streamed(args):
         avail = 64 << 30
     n_blobs = int(max(2, min(L, (0.5 * avail) // nbytes)))
     t0 = time.time()
+    # pinned blobs on the GPU's NUMA node when the host has several
+    import glob as _glob
+    host_nodes = len(_glob.glob("/sys/devices/system/node/node[0-9]*")) or 1
+    gnode = gpu_numa_node()
+    numa_bound = host_nodes > 1 and gnode >= 0 and prefer_numa_node(gnode)
     blobs = []
     for b in range(n_blobs):
         try:
@@ -644,7 +699,13 @@ def bench_streamed(args):
         if b % 4 == 3 or b == n_blobs - 1:
             log(f"[bench] streamed: {b + 1}/{n_blobs} pinned blobs filled ({time.time() - t0:.1f}s)")
     torch.cuda.synchronize()
-    log(f"[bench] streamed: {n_blobs} pinned blobs of {nbytes / 1e9:.3f} GB in {time.time() - t0:.1f}s")
+    if numa_bound:
+        prefer_numa_node(-1)
+    page_nodes = sorted(set(n for b in blobs for n in page_numa_nodes(b)))
+    numa = {"host_nodes": host_nodes, "gpu_node": gnode, "policy": "preferred gpu node" if numa_bound else
+            ("single node: every page is local" if host_nodes == 1 else "gpu node unknown: default policy"),
+            "blob_page_nodes": page_nodes}
+    log(f"[bench] streamed: {n_blobs} pinned blobs of {nbytes / 1e9:.3f} GB in {time.time() - t0:.1f}s; numa {numa}")
     slots = [torch.empty(nbytes, dtype=torch.uint8, device=dev) for _ in range(2)]
     logits = torch.from_numpy(np.stack([gen.router_logits(shape, l) for l in range(L)])).to(dev)
     x = gen.activations_bf16(shape).to(dev)
@@ -744,7 +805,7 @@ def bench_streamed(args):
         "warmup": args.warmup, "ms_per_step": ms, "higher_is_better": True, "scaling": "weak",
         "vs_baseline": None, "dtype": "bf16xmxfp4", "data": "synthetic",
         "config": {"workload": "streamed", "layers": L, "T": T, "hidden": H, "intermediate": I, "experts": E,
-                   "top_k": k, "distinct_host_blobs": n_blobs, "blob_GB": nbytes / 1e9,
+                   "top_k": k, "distinct_host_blobs": n_blobs, "blob_GB": nbytes / 1e9, "numa": numa,
                    "expert_copy": args.expert_copy, "parallelism": "none (1 GPU)"},
         "experts_hit_per_layer_mean": float(np.mean(hits)), "h2d_bytes_per_pass": h2d_bytes,
         "all_experts_ms": all_ms,
