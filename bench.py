@@ -491,11 +491,12 @@ def _counter_rows(d):
 
 
 def _gemm_call(kernel_name):
-    """'fc1' / 'fc2' for a grouped-GEMM class kernel (epilogue template argument 1 / 0), else None."""
-    for tag in ("gemm_dma_kernel<", "gemm_kernel<"):
+    """'fc1' / 'fc2' for a grouped-GEMM kernel (its epilogue template argument: SwiGLU 1 / plain 0), else None.
+    gemm_dma_kernel / gemm_kernel take <BM, FP8, EPI, ...>, gemm_mixed_kernel <FP8, EPI, OUT>."""
+    for tag, epi_arg in (("gemm_dma_kernel<", 2), ("gemm_kernel<", 2), ("gemm_mixed_kernel<", 1)):
         if tag in kernel_name:
             targs = kernel_name.split(tag, 1)[1].split(">", 1)[0].split(",")
-            return "fc1" if int(targs[2]) != 0 else "fc2"
+            return "fc1" if int(targs[epi_arg]) != 0 else "fc2"
     return None
 
 

@@ -38,7 +38,11 @@
 // K [32+16g, 32+16g+16), and the E8M0 scale supplied by a lane in half g
 // applies to K block g of its row/column.  For the bf16 32x32x16 MFMA a
 // lane in half g holds K [8g, 8g+8).  Accumulator j of lane l is
-// C[8*(j/4) + 4*(l/32) + j%4][l % 32].
+// C[8*(j/4) + 4*(l/32) + j%4][l % 32].  The two operands share that lane
+// layout, so the DMA kernels, which pass the weights as the first operand and
+// the activations as the second, accumulate the transposed tile: lane l owns
+// one output row, which makes the per-row MX block amax of the MXFP8 epilogue
+// one exchange with the partner lane l ^ 32.
 #include <type_traits>
 
 #include "internal.h"
@@ -451,6 +455,35 @@ __device__ __forceinline__ void dma16(__amdgpu_buffer_rsrc_t r, uint32_t voff, u
   __builtin_amdgcn_raw_ptr_buffer_load_lds(r, (__attribute__((address_space(3))) void*)dst, 16, voff, soff, 0, 0);
 }
 
+// This lane's index in its wave, in a fresh register each call: an opaque
+// value (the compiler cannot hoist what is derived from it) that, unlike a
+// copy of the thread index, keeps no register live between its uses.
+__device__ __forceinline__ int lane_id() {
+  int l;
+  asm volatile("v_mbcnt_lo_u32_b32 %0, -1, 0\n\tv_mbcnt_hi_u32_b32 %0, -1, %0" : "=v"(l));
+  return l;
+}
+
+// LDS byte address of a pointer into this block's LDS
+__device__ __forceinline__ uint32_t lds_addr(const void* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) void*)p;
+}
+
+// LDS reads for code that runs while DMA into other LDS buffers is in flight:
+// the compiler orders a plain LDS read after every outstanding LDS DMA (it
+// cannot tell the buffers apart); these reads are outside its view, so each
+// waits for its own data before it returns.
+__device__ __forceinline__ uint4 lds_read16(uint32_t addr) {
+  uint4 v;
+  asm volatile("ds_read_b128 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+__device__ __forceinline__ uint32_t lds_read4(uint32_t addr) {
+  uint32_t v;
+  asm volatile("ds_read_b32 %0, %1\n\ts_waitcnt lgkmcnt(0)" : "=v"(v) : "v"(addr) : "memory");
+  return v;
+}
+
 template <int N>
 __device__ __forceinline__ void wait_vm() {
   static_assert(N >= 0 && N < 64, "vmcnt range");
@@ -501,587 +534,697 @@ __device__ inline int mxfp8_block_exp(float amax) {
   return x < -127 ? -127 : (x > 127 ? 127 : x);
 }
 
-// One persistent block walks (tile, n-tile) units.  Per unit, the K loop runs
-// over 128-element stages through three LDS stage buffers filled by DMA two
-// stages ahead.  FP8 operands: the stage's fragments are read into registers
-// half a stage ahead of their products (second k-half during the first
-// half's MFMAs, next stage's first k-half during the second half's), with
-// one barrier in the middle of each stage that both publishes stage s+1 and
-// frees stage s's buffer for the DMA of stage s+3.  bf16 operands: the
-// stage's reads and products follow one barrier at its start.
-// One unit (row tile x 256-column n-tile) of a grouped GEMM class: the DMA
-// pipeline over K and the epilogue.  tid_in: the thread's index within the
-// NW waves that run the unit; lds: their LDS area (Cfg2<BM, FP8, NW>::LDS_TOTAL
-// bytes); store: false runs the unit without writing C (a block that runs two
-// units side by side keeps both halves in step with one).  Every wave of the
-// block executes the same barriers.
-template <int BM, bool FP8, int EPI, int OUT, bool TILED, int NW>
-__device__ __forceinline__ void run_unit(const Params& p, int u, int count, int tid_in, uint8_t* lds, bool store) {
+// Output staging of one unit.  The accumulators hold the transposed tile
+// (see the epilogue); MXFP8 output stages its E4M3 codes (one byte an
+// element, quantised in registers) and each row's E8M0 bytes, bf16 output
+// its values, fp32 output goes straight to memory.  A tile whose staging
+// would cover more than two stage buffers is staged in row passes of whole
+// waves, so that at least one stage buffer stays free while the epilogue
+// runs.  The staging sits in the last USED stage buffers (from byte offset
+// BASE on); the next unit's first PF stages go to buffers 0 .. PF-1, where
+// they belong.
+template <int BM, bool FP8, int EPI, int OUT, int NW>
+struct EpiCfg {
   using C = Cfg2<BM, FP8, NW>;
+  static constexpr bool MX = OUT == MOE_OUT_MXFP8_E4M3;
+  static constexpr bool STAGED = OUT != MOE_OUT_FP32;
+  static constexpr int TC = EPI == 0 ? kBN : kBN / 2;         // output columns of a tile
+  static constexpr int PITCH = MX ? TC + 16 : 2 * TC + 16;    // staged bytes per row (16-byte pad)
+  static constexpr int ROW_BYTES = MX ? PITCH + TC / 32 : PITCH;
+  static constexpr int PASSES = !STAGED ? 0
+                                : BM * ROW_BYTES <= 2 * C::LDS_STAGE       ? 1
+                                : BM / 2 * ROW_BYTES <= 2 * C::LDS_STAGE   ? 2
+                                                                           : 4;
+  static constexpr int PROWS = STAGED ? BM / PASSES : 0;       // rows of one pass
+  static constexpr int SC_OFF = PROWS * PITCH;                 // MXFP8: the rows' E8M0 bytes
+  static constexpr int USED = (PROWS * ROW_BYTES + C::LDS_STAGE - 1) / C::LDS_STAGE;   // buffers staging covers
+  static constexpr int PF = C::NST - USED;
+  // whether the next unit's set-up and first PF stages start during the
+  // epilogue (the eight-wave plain-output tiles keep no registers to spare
+  // for the next unit's DMA offsets there: they start it after the epilogue)
+  static constexpr bool EARLY = !(EPI == 0 && NW == 8);
+  static constexpr int BASE = PF * C::LDS_STAGE;
+  static_assert(!STAGED || (PASSES <= C::WAVES_M && C::WAVES_M % PASSES == 0), "passes of whole waves' rows");
+  static_assert(PF >= 1, "a stage buffer stays free during the epilogue");
+  static_assert(BASE + PROWS * ROW_BYTES <= C::NST * C::LDS_STAGE, "the staging stays within the stage buffers");
+};
+
+// One persistent block walks (tile, n-tile) units of one row-tile class: unit
+// u, then the units next() returns (the same value in every thread; < 0: no
+// more).  Per unit, the K loop runs over 128-element stages through three LDS
+// stage buffers filled by DMA two stages ahead.  FP8 operands: the stage's
+// fragments are read into registers half a stage ahead of their products
+// (second k-half during the first half's MFMAs, next stage's first k-half
+// during the second half's), with one barrier in the middle of each stage
+// that both publishes stage s+1 and frees stage s's buffer for the DMA of
+// stage s+3.  bf16 operands: the stage's reads and products follow one
+// barrier at its start.  Between two units the next unit's scale group 0 and
+// its first PF stages are issued into the LDS the epilogue's staging leaves
+// free, once the staging is written and before it is read back and stored, so
+// that their latency passes under the stores; its other stages follow the
+// epilogue.
+// next() may issue the block's following draw; settle(), called after each
+// epilogue, takes its result.  tid_in: the thread's index within the NW waves
+// that run the units; lds:
+// their LDS area (Cfg2<BM, FP8, NW>::LDS_TOTAL bytes); store: false runs the
+// units without writing C (a block that runs two units side by side keeps
+// both halves in step with one).  Every wave of the block executes the same
+// barriers, next() included.
+template <int BM, bool FP8, int EPI, int OUT, bool TILED, int NW, typename Next, typename Settle>
+__device__ __forceinline__ void run_units(const Params& p, int u, int count, int tid_in, uint8_t* lds, bool store,
+                                          Next&& next, Settle&& settle) {
+  using C = Cfg2<BM, FP8, NW>;
+  using EC = EpiCfg<BM, FP8, EPI, OUT, NW>;
   const int K = p.K;
   const int a_row_bytes = FP8 ? K : 2 * K;
   const int kb = K / 32;
   const int nst = K / C::KS;
-
-  // Lane-derived values are recomputed per unit from an opaque copy of the
-  // thread index.  Hoisted out of the unit loop they stay live across it and
-  // get spilled, and a spill reload in the pipeline prologue would wait for
-  // every DMA in flight.
-  int tid;
-  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid_in));
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm0 = (wave / C::WAVES_N) * C::WM;
-  const int wn0 = (wave % C::WAVES_N) * C::WN;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-  // 32-column block of the tile that B fragment j of this wave reads.  Tile
+  // 32-column block of the tile that B fragment j of a wave reads.  Tile
   // columns come in groups of 64 (32 gate rows, then their 32 up rows) for
   // every tile class; the wave's fragments are ordered even blocks first, so
   // that with a SwiGLU epilogue fragment fh (gate) and fh + FN/2 (up) pair
-  // up.  Without one the epilogue writes the same pairs side by side: that
+  // up.  Without one the epilogue stages the same pairs side by side: that
   // order is also what keeps the eight-wave FC2 tile free of spills (its
   // identity order spilled 24-33 VGPRs of DMA offsets and LDS addresses
   // inside the K loop).
   auto frag_block = [](int j) { return (j % (C::FN / 2)) * 2 + j / (C::FN / 2); };
-  // fragment rows / lines start at multiples of 16, so the swizzles depend on the lane only
-  const int xa = a_swz<FP8>(l32 & 15);
-  const int xb = b_swz((l32 >> 1) & 7);
-
-  // units in groups of up to 4 row tiles x all n-tiles, row tile fastest, so
-  // that concurrent blocks of one XCD share both their A rows and their B tiles
-  constexpr int GM = 4;
-  const int grp = u / (GM * p.n_tiles);
-  const int first = grp * GM;
-  const int gsize = min(GM, count - first);
-  const int in = u - grp * GM * p.n_tiles;
-  const int ti = first + in % gsize;
-  const int nt = in / gsize;
-  const Tile tile = p.tiles[ti];
-  const int e = tile.expert;
-  const int row0 = tile.row0;
-  const int mrows = min(BM, p.offsets[e + 1] - row0);
-  const size_t w_expert = (size_t)e * p.N;
-
-  // ---- DMA sources: uniform bases, 32-bit per-lane byte offsets (stage 0) ----
-  // gathered A rows: offsets from the start of A; contiguous A rows: from the tile's first row
-  const bool gather = p.a_gather != nullptr;
-  const uint8_t* const a_base = gather ? p.a : p.a + (size_t)row0 * a_row_bytes;
-  uint32_t a_off[C::A_I];
-  {
-    int arow[C::A_I];
-#pragma unroll
-    for (int i = 0; i < C::A_I; ++i)
-      arow[i] = min((wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA, mrows - 1);
-    if (gather) {
-      // all index loads in flight together
-#pragma unroll
-      for (int i = 0; i < C::A_I; ++i) arow[i] = p.a_gather[row0 + arow[i]];
-#pragma unroll
-      for (int i = 0; i < C::A_I; ++i) arow[i] /= p.a_gather_div;
-    }
-#pragma unroll
-    for (int i = 0; i < C::A_I; ++i) {
-      const int r = (wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA;
-      const int chunk = (lane % C::SA) ^ a_swz<FP8>(r);
-      a_off[i] = (uint32_t)arow[i] * (uint32_t)a_row_bytes + chunk * 16;
-    }
-  }
-  // B: canonical weights are addressed row by row (tile column j of the
-  // stage's LDS layout <- its weight row); tiled weights already hold the
-  // stage's 16 KB in LDS order, so each instruction copies 1 KB of
-  // consecutive bytes.  b_step / bs_step: bytes from one stage (one scale
-  // group) to the next.
-  const size_t tile_id = (size_t)e * p.n_tiles + nt;
-  const uint8_t* const b_base = TILED ? p.w + tile_id * (size_t)nst * C::LDS_B : p.w + w_expert * (size_t)(K / 2);
-  const int b_step = TILED ? C::LDS_B : C::RB;
-  uint32_t b_off[C::B_I];
-#pragma unroll
-  for (int i = 0; i < C::B_I; ++i) {
-    const int line = (wave * C::B_I + i) * 8 + lane / 8;
-    const int uu = (lane & 7) ^ b_swz(line);
-    const int j = line * 2 + (uu >> 2);
-    const int wr = w_row_of<kSwiGroup>(p.layout, nt, j, p.N, p.n_out);
-    b_off[i] = TILED ? (uint32_t)((wave * C::B_I + i) * 1024 + lane * 16)
-                         : (uint32_t)wr * (uint32_t)(K / 2) + (uu & 3) * 16;
-  }
-  // scale loads: with four waves every wave loads 64 rows of A scales (if
-  // below BM) and 64 of B scales; with eight, waves 0-3 load A, 4-7 load B
-  const bool a_sw = C::NW == 8 ? wave < 4 : true;
-  const bool b_sw = C::NW == 8 ? wave >= 4 : true;
-  const int sw = (C::NW == 8 && wave >= 4) ? wave - 4 : wave;
-  const int srow = sw * 64 + lane;   // scale row this lane loads (A: if < BM)
-  const uint8_t* const as_base = gather ? p.a_scales : p.a_scales + (size_t)row0 * kb;
-  uint32_t as_off = 0;
-  if (FP8 && a_sw && srow < BM) {
-    const int r = min(srow, mrows - 1);
-    as_off = (uint32_t)(gather ? p.a_gather[row0 + r] / p.a_gather_div : r) * (uint32_t)kb;
-  }
-  const uint8_t* const bs_base =
-      TILED ? p.w_scales + tile_id * (size_t)(K / 512) * 4096 : p.w_scales + w_expert * (size_t)kb;
-  const int bs_step = TILED ? 4096 : 16;
-  const uint32_t bs_off = TILED ? (uint32_t)(sw * 1024 + lane * 16)
-                                    : (uint32_t)w_row_of<kSwiGroup>(p.layout, nt, srow, p.N, p.n_out) * (uint32_t)kb;
   uint8_t* const sg = lds + C::NST * C::LDS_STAGE;   // two scale groups
 
-  const __amdgpu_buffer_rsrc_t ra = make_rsrc(a_base);
-  const __amdgpu_buffer_rsrc_t rb = make_rsrc(b_base);
-  const __amdgpu_buffer_rsrc_t ras = make_rsrc(as_base);
-  const __amdgpu_buffer_rsrc_t rbs = make_rsrc(bs_base);
-  auto issue = [&](int s) {
-    uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
+  // ---- DMA state of the unit whose stages are in flight (set by setup) ----
+  int row0 = 0, mrows = 0, nt = 0;
+  uint32_t a_off[C::A_I], b_off[C::B_I], as_off = 0, bs_off = 0;
+  __amdgpu_buffer_rsrc_t ra, rb, ras, rbs;
+  // scale loads: with four waves every wave loads 64 rows of A scales (if
+  // below BM) and 64 of B scales; with eight, waves 0-3 load A, 4-7 load B
+  const int wave_u = __builtin_amdgcn_readfirstlane(tid_in >> 6);
+  const bool a_sw = C::NW == 8 ? wave_u < 4 : true;
+  const bool b_sw = C::NW == 8 ? wave_u >= 4 : true;
+  const int sw = (C::NW == 8 && wave_u >= 4) ? wave_u - 4 : wave_u;
+
+  // Lane-derived values are recomputed wherever they are used, from
+  // lane_id() and the wave index (a scalar).  Hoisted out of the unit loop
+  // they stay live across it and get spilled, and a spill reload waits for
+  // every DMA in flight.
+  auto setup = [&](int uu) {
+    const int lane = lane_id();
+    const int wave = wave_u;
+    // units in groups of up to 4 row tiles x all n-tiles, row tile fastest, so
+    // that concurrent blocks of one XCD share both their A rows and their B tiles
+    constexpr int GM = 4;
+    const int grp = uu / (GM * p.n_tiles);
+    const int first = grp * GM;
+    const int gsize = min(GM, count - first);
+    const int in = uu - grp * GM * p.n_tiles;
+    const int ti = first + in % gsize;
+    nt = in / gsize;
+    const Tile tile = p.tiles[ti];
+    const int e = tile.expert;
+    row0 = tile.row0;
+    mrows = min(BM, p.offsets[e + 1] - row0);
+    const size_t w_expert = (size_t)e * p.N;
+
+    // DMA sources: uniform bases, 32-bit per-lane byte offsets (stage 0).
+    // Gathered A rows: offsets from the start of A; contiguous A rows: from the tile's first row.
+    const bool gather = p.a_gather != nullptr;
+    const uint8_t* const a_base = gather ? p.a : p.a + (size_t)row0 * a_row_bytes;
+    {
+      int arow[C::A_I];
 #pragma unroll
-    for (int i = 0; i < C::A_I; ++i) dma16(ra, a_off[i], s * C::RA, base + (wave * C::A_I + i) * 1024);
+      for (int i = 0; i < C::A_I; ++i)
+        arow[i] = min((wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA, mrows - 1);
+      if (gather) {
+        // all index loads in flight together
+#pragma unroll
+        for (int i = 0; i < C::A_I; ++i) arow[i] = p.a_gather[row0 + arow[i]];
+#pragma unroll
+        for (int i = 0; i < C::A_I; ++i) arow[i] /= p.a_gather_div;
+      }
+#pragma unroll
+      for (int i = 0; i < C::A_I; ++i) {
+        const int r = (wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA;
+        const int chunk = (lane % C::SA) ^ a_swz<FP8>(r);
+        a_off[i] = (uint32_t)arow[i] * (uint32_t)a_row_bytes + chunk * 16;
+      }
+    }
+    // B: canonical weights are addressed row by row (tile column j of the
+    // stage's LDS layout <- its weight row); tiled weights already hold the
+    // stage's 16 KB in LDS order, so each instruction copies 1 KB of
+    // consecutive bytes.
+    const size_t tile_id = (size_t)e * p.n_tiles + nt;
+    const uint8_t* const b_base = TILED ? p.w + tile_id * (size_t)nst * C::LDS_B : p.w + w_expert * (size_t)(K / 2);
+#pragma unroll
+    for (int i = 0; i < C::B_I; ++i) {
+      const int line = (wave * C::B_I + i) * 8 + lane / 8;
+      const int uu2 = (lane & 7) ^ b_swz(line);
+      const int j = line * 2 + (uu2 >> 2);
+      const int wr = w_row_of<kSwiGroup>(p.layout, nt, j, p.N, p.n_out);
+      b_off[i] = TILED ? (uint32_t)((wave * C::B_I + i) * 1024 + lane * 16)
+                       : (uint32_t)wr * (uint32_t)(K / 2) + (uu2 & 3) * 16;
+    }
+    const int srow = sw * 64 + lane;   // scale row this lane loads (A: if < BM)
+    const uint8_t* const as_base = gather ? p.a_scales : p.a_scales + (size_t)row0 * kb;
+    as_off = 0;
+    if (FP8 && a_sw && srow < BM) {
+      const int r = min(srow, mrows - 1);
+      as_off = (uint32_t)(gather ? p.a_gather[row0 + r] / p.a_gather_div : r) * (uint32_t)kb;
+    }
+    const uint8_t* const bs_base =
+        TILED ? p.w_scales + tile_id * (size_t)(K / 512) * 4096 : p.w_scales + w_expert * (size_t)kb;
+    bs_off = TILED ? (uint32_t)(sw * 1024 + lane * 16)
+                   : (uint32_t)w_row_of<kSwiGroup>(p.layout, nt, srow, p.N, p.n_out) * (uint32_t)kb;
+    ra = make_rsrc(a_base);
+    rb = make_rsrc(b_base);
+    ras = make_rsrc(as_base);
+    rbs = make_rsrc(bs_base);
+  };
+  // b_step / bs_step: bytes from one stage (one scale group) to the next
+  const int b_step = TILED ? C::LDS_B : C::RB;
+  const int bs_step = TILED ? 4096 : 16;
+  auto stage_at = [&](int s) { return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE); };
+  auto issue = [&](int s) {
+    uint8_t* base = stage_at(s);
+#pragma unroll
+    for (int i = 0; i < C::A_I; ++i) dma16(ra, a_off[i], s * C::RA, base + (wave_u * C::A_I + i) * 1024);
 #pragma unroll
     for (int i = 0; i < C::B_I; ++i)
-      dma16(rb, b_off[i], s * b_step, base + C::LDS_A + (wave * C::B_I + i) * 1024);
+      dma16(rb, b_off[i], s * b_step, base + C::LDS_A + (wave_u * C::B_I + i) * 1024);
   };
   // DMA instruction j of stage s (j < A_I: A, then B), for interleaving with products
   auto issue_one = [&](int s, int j) {
-    uint8_t* base = lds + (s % C::NST) * C::LDS_STAGE;
-    if (j < C::A_I) dma16(ra, a_off[j], s * C::RA, base + (wave * C::A_I + j) * 1024);
-    else dma16(rb, b_off[j - C::A_I], s * b_step, base + C::LDS_A + (wave * C::B_I + j - C::A_I) * 1024);
+    uint8_t* base = stage_at(s);
+    if (j < C::A_I) dma16(ra, a_off[j], s * C::RA, base + (wave_u * C::A_I + j) * 1024);
+    else dma16(rb, b_off[j - C::A_I], s * b_step, base + C::LDS_A + (wave_u * C::B_I + j - C::A_I) * 1024);
   };
   // scale group j (stages 4j..4j+3): 16 bytes of every A and B row
   auto issue_scales = [&](int j) {
     uint8_t* base = sg + (j & 1) * C::LDS_SG;
     // (a 32-row tile has 512 bytes of A scales per group: lanes 32-63 stay idle)
-    if (FP8 && a_sw && sw * 64 < BM && (BM >= 64 || lane < BM)) dma16(ras, as_off, 16 * j, base + sw * 1024);
+    if (FP8 && a_sw && sw * 64 < BM && (BM >= 64 || lane_id() < BM)) dma16(ras, as_off, 16 * j, base + sw * 1024);
     if (b_sw) dma16(rbs, bs_off, bs_step * j, base + C::SG_A + sw * 1024);
   };
 
-  v16f acc[C::FM][C::FN];
-#pragma unroll
-  for (int i = 0; i < C::FM; ++i)
-#pragma unroll
-    for (int j = 0; j < C::FN; ++j)
-#pragma unroll
-      for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+  setup(__builtin_amdgcn_readfirstlane(u));
+  issue_scales(0);
+  issue(0);
+  issue(1);
+  issue(2);
+  for (;;) {
+    const int lane = lane_id();
+    const int wave = wave_u;
+    const int wm0 = (wave / C::WAVES_N) * C::WM;
+    const int wn0 = (wave % C::WAVES_N) * C::WN;
+    const int l32 = lane & 31;
+    const int g = lane >> 5;
+    // fragment rows / lines start at multiples of 16, so the swizzles depend on the lane only
+    const int xa = a_swz<FP8>(l32 & 15);
+    const int xb = b_swz((l32 >> 1) & 7);
 
-  if constexpr (FP8) {
-    uint32_t sa[C::FM], sb[C::FN], na[C::FM], nb[C::FN];
-    v8i a0[C::FM], a1[C::FM];
-    v4i b0[C::FN], b1[C::FN];
-    // LDS base of stage s, made opaque to the compiler: otherwise every
-    // fragment address becomes an induction variable of its own
-    auto stage_lds = [&](int s) {
-      return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
-    };
-    // read j of one k-half: j < FN: B fragment j; then the A fragments' low and high halves
-    // (A: K [kk*64 + 16g, +16) and [kk*64 + 32 + 16g, +16) = chunks 4kk+g and 4kk+2+g)
-    auto read_frag = [&](int s, int kk, int j, v8i (&af)[C::FM], v4i (&bq)[C::FN]) {
-      const uint8_t* la = stage_lds(s);
-      if (j < C::FN) {
-        const int n = wn0 + frag_block(j) * 32 + l32;
-        const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xb;
-        bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
-      } else {
-        const int fm = (j - C::FN) >> 1, hi = (j - C::FN) & 1;
-        const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
-        const v4i v = *reinterpret_cast<const v4i*>(row + (((4 * kk + 2 * hi + g) ^ xa) << 4));
-        if (hi) {
-          af[fm][4] = v[0]; af[fm][5] = v[1]; af[fm][6] = v[2]; af[fm][7] = v[3];
+    v16f acc[C::FM][C::FN];
+#pragma unroll
+    for (int i = 0; i < C::FM; ++i)
+#pragma unroll
+      for (int j = 0; j < C::FN; ++j)
+#pragma unroll
+        for (int q = 0; q < 16; ++q) acc[i][j][q] = 0.f;
+
+    if constexpr (FP8) {
+      uint32_t sa[C::FM], sb[C::FN], na[C::FM], nb[C::FN];
+      v8i a0[C::FM], a1[C::FM];
+      v4i b0[C::FN], b1[C::FN];
+      // LDS base of stage s, made opaque to the compiler: otherwise every
+      // fragment address becomes an induction variable of its own
+      auto stage_lds = [&](int s) {
+        return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
+      };
+      // read j of one k-half: j < FN: B fragment j; then the A fragments' low and high halves
+      // (A: K [kk*64 + 16g, +16) and [kk*64 + 32 + 16g, +16) = chunks 4kk+g and 4kk+2+g)
+      auto read_frag = [&](int s, int kk, int j, v8i (&af)[C::FM], v4i (&bq)[C::FN]) {
+        const uint8_t* la = stage_lds(s);
+        if (j < C::FN) {
+          const int n = wn0 + frag_block(j) * 32 + l32;
+          const int uu = ((n & 1) * 4 + 2 * kk + g) ^ xb;
+          bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
         } else {
-          af[fm][0] = v[0]; af[fm][1] = v[1]; af[fm][2] = v[2]; af[fm][3] = v[3];
+          const int fm = (j - C::FN) >> 1, hi = (j - C::FN) & 1;
+          const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
+          const v4i v = *reinterpret_cast<const v4i*>(row + (((4 * kk + 2 * hi + g) ^ xa) << 4));
+          if (hi) {
+            af[fm][4] = v[0]; af[fm][5] = v[1]; af[fm][6] = v[2]; af[fm][7] = v[3];
+          } else {
+            af[fm][0] = v[0]; af[fm][1] = v[1]; af[fm][2] = v[2]; af[fm][3] = v[3];
+          }
         }
-      }
-    };
-    // scale word j of stage s: four E8M0 bytes (the stage's blocks) of an A row or B column
-    auto read_scale = [&](int s, int j, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
-      const uint8_t* lsg = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4);
-      if (j < C::FM) ta[j] = *reinterpret_cast<const uint32_t*>(lsg + (wm0 + j * 32 + l32) * 16);
-      else tb[j - C::FM] = *reinterpret_cast<const uint32_t*>(lsg + C::SG_A + (wn0 + frag_block(j - C::FM) * 32 + l32) * 16);
-    };
-    // product i of one k-half, B-fragment major.  ta/tb hold this lane's scale
-    // bytes in the order the op_sel field reads them: byte kk = block 2kk + g.
-    auto mma = [&](int kk, int i, const v8i (&af)[C::FM], const v4i (&bq)[C::FN], const uint32_t (&ta)[C::FM],
-                   const uint32_t (&tb)[C::FN]) {
-      const int fn = i / C::FM, fm = i % C::FM;
-      const v8i bf = v8i{bq[fn][0], bq[fn][1], bq[fn][2], bq[fn][3], 0, 0, 0, 0};
-      if (kk == 0)
-        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0 /*A: fp8 e4m3*/,
-                                                                      4 /*B: fp4 e2m1*/, 0, ta[fm], 0, tb[fn]);
-      else
-        acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(af[fm], bf, acc[fm][fn], 0, 4, 1, ta[fm],
-                                                                      1, tb[fn]);
-    };
-    // a stage's four scale bytes (blocks 0..3) -> this lane's two, in op_sel order
-    const uint32_t scale_sel = g ? 0x0c0c0301u : 0x0c0c0200u;
-    auto order_scales = [&](uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
+      };
+      // scale word j of stage s: four E8M0 bytes (the stage's blocks) of an A row or B column
+      auto read_scale = [&](int s, int j, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
+        const uint8_t* lsg = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4);
+        if (j < C::FM) ta[j] = *reinterpret_cast<const uint32_t*>(lsg + (wm0 + j * 32 + l32) * 16);
+        else tb[j - C::FM] = *reinterpret_cast<const uint32_t*>(lsg + C::SG_A + (wn0 + frag_block(j - C::FM) * 32 + l32) * 16);
+      };
+      // product i of one k-half, B-fragment major.  ta/tb hold this lane's scale
+      // bytes in the order the op_sel field reads them: byte kk = block 2kk + g.
+      // The weights are the instruction's first operand and the activations its
+      // second, so the accumulator holds the transposed tile (see the epilogue).
+      auto mma = [&](int kk, int i, const v8i (&af)[C::FM], const v4i (&bq)[C::FN], const uint32_t (&ta)[C::FM],
+                     const uint32_t (&tb)[C::FN]) {
+        const int fn = i / C::FM, fm = i % C::FM;
+        const v8i bf = v8i{bq[fn][0], bq[fn][1], bq[fn][2], bq[fn][3], 0, 0, 0, 0};
+        if (kk == 0)
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af[fm], acc[fm][fn], 4 /*fp4 e2m1*/,
+                                                                        0 /*fp8 e4m3*/, 0, tb[fn], 0, ta[fm]);
+        else
+          acc[fm][fn] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(bf, af[fm], acc[fm][fn], 4, 0, 1, tb[fn],
+                                                                        1, ta[fm]);
+      };
+      // a stage's four scale bytes (blocks 0..3) -> this lane's two, in op_sel order
+      const uint32_t scale_sel = g ? 0x0c0c0301u : 0x0c0c0200u;
+      auto order_scales = [&](uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN]) {
 #pragma unroll
-      for (int j = 0; j < C::FM; ++j) ta[j] = __builtin_amdgcn_perm(0u, ta[j], scale_sel);
+        for (int j = 0; j < C::FM; ++j) ta[j] = __builtin_amdgcn_perm(0u, ta[j], scale_sel);
 #pragma unroll
-      for (int j = 0; j < C::FN; ++j) tb[j] = __builtin_amdgcn_perm(0u, tb[j], scale_sel);
-    };
-    constexpr int MF = C::FM * C::FN;
-    constexpr int NR = 2 * C::FM + C::FN;   // fragment reads of one k-half
-    constexpr int NS = C::FM + C::FN;       // scale reads of one stage
-    // reads issued after each product: at least two (front-loaded), more for small tiles
-    constexpr int R1 = (NR + MF - 1) / MF > 2 ? (NR + MF - 1) / MF : 2;
-    constexpr int R2 = (NR + NS + MF - 1) / MF > 2 ? (NR + NS + MF - 1) / MF : 2;
-    constexpr int D2 = (C::LOADS + MF - 1) / MF;   // refill DMA instructions per product
-    // One stage.  ISSUE: refill the freed buffer with stage s+3 during the second
-    // half (SCALES: and the next scale group); WAIT: vmcnt allowance at the
-    // mid-stage barrier, -1 for the last stage (no barrier, no next-stage
-    // reads).  All three are compile-time constants so that the loop body has
-    // no branch the compiler could sink the first half's products past.  Every
-    // group of one product and its reads / DMA is fenced with sched_barrier to
-    // keep the interleave.
-    auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN],
-                    uint32_t (&tna)[C::FM], uint32_t (&tnb)[C::FN]) {
-      constexpr bool kIssue = decltype(ISSUE)::value;
-      constexpr bool kScales = decltype(SCALES)::value;
-      constexpr int kWait = decltype(WAIT)::value;
-      order_scales(ta, tb);
+        for (int j = 0; j < C::FN; ++j) tb[j] = __builtin_amdgcn_perm(0u, tb[j], scale_sel);
+      };
+      constexpr int MF = C::FM * C::FN;
+      constexpr int NR = 2 * C::FM + C::FN;   // fragment reads of one k-half
+      constexpr int NS = C::FM + C::FN;       // scale reads of one stage
+      // reads issued after each product: at least two (front-loaded), more for small tiles
+      constexpr int R1 = (NR + MF - 1) / MF > 2 ? (NR + MF - 1) / MF : 2;
+      constexpr int R2 = (NR + NS + MF - 1) / MF > 2 ? (NR + NS + MF - 1) / MF : 2;
+      constexpr int D2 = (C::LOADS + MF - 1) / MF;   // refill DMA instructions per product
+      // One stage.  ISSUE: refill the freed buffer with stage s+3 during the second
+      // half (SCALES: and the next scale group); WAIT: vmcnt allowance at the
+      // mid-stage barrier, -1 for the last stage (no barrier, no next-stage
+      // reads).  All three are compile-time constants so that the loop body has
+      // no branch the compiler could sink the first half's products past.  Every
+      // group of one product and its reads / DMA is fenced with sched_barrier to
+      // keep the interleave.
+      auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&ta)[C::FM], uint32_t (&tb)[C::FN],
+                      uint32_t (&tna)[C::FM], uint32_t (&tnb)[C::FN]) {
+        constexpr bool kIssue = decltype(ISSUE)::value;
+        constexpr bool kScales = decltype(SCALES)::value;
+        constexpr int kWait = decltype(WAIT)::value;
+        order_scales(ta, tb);
 #pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        mma(0, i, a0, b0, ta, tb);
-        __builtin_amdgcn_sched_barrier(0);
+        for (int i = 0; i < MF; ++i) {
+          mma(0, i, a0, b0, ta, tb);
+          __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int r = R1 * i; r < R1 * i + R1; ++r)
-          if (r < NR) read_frag(s, 1, r, a1, b1);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-      // the first half's products stay ahead of the barrier
+          for (int r = R1 * i; r < R1 * i + R1; ++r)
+            if (r < NR) read_frag(s, 1, r, a1, b1);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+        // the first half's products stay ahead of the barrier
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+        for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
-      if constexpr (kWait >= 0) {
-        // stage s fully read by this wave; stage s+1 landed for this wave's loads
-        wait_lgkm0();
-        wait_vm<kWait>();
-        stage_barrier();
-      }
-      __builtin_amdgcn_sched_barrier(0);
-#pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        mma(1, i, a1, b1, ta, tb);
-        __builtin_amdgcn_sched_barrier(0);
+          for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
         if constexpr (kWait >= 0) {
-#pragma unroll
-          for (int r = R2 * i; r < R2 * i + R2; ++r) {
-            if (r < NS) read_scale(s + 1, r, tna, tnb);
-            else if (r < NS + NR) read_frag(s + 1, 0, r - NS, a0, b0);
-          }
-        }
-        // the refill of the freed buffer (stage s+3), spread over the products
-        if constexpr (kIssue) {
-#pragma unroll
-          for (int j = D2 * i; j < D2 * i + D2; ++j) {
-            if (j < C::LOADS) issue_one(s + 3, j);
-            if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
-          }
+          // stage s fully read by this wave; stage s+1 landed for this wave's loads
+          wait_lgkm0();
+          wait_vm<kWait>();
+          stage_barrier();
         }
         __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < MF; ++i) {
+          mma(1, i, a1, b1, ta, tb);
+          __builtin_amdgcn_sched_barrier(0);
+          if constexpr (kWait >= 0) {
+#pragma unroll
+            for (int r = R2 * i; r < R2 * i + R2; ++r) {
+              if (r < NS) read_scale(s + 1, r, tna, tnb);
+              else if (r < NS + NR) read_frag(s + 1, 0, r - NS, a0, b0);
+            }
+          }
+          // the refill of the freed buffer (stage s+3), spread over the products
+          if constexpr (kIssue) {
+#pragma unroll
+            for (int j = D2 * i; j < D2 * i + D2; ++j) {
+              if (j < C::LOADS) issue_one(s + 3, j);
+              if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
+            }
+          }
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      using T = std::integral_constant<bool, true>;
+      using F = std::integral_constant<bool, false>;
+      using WL = std::integral_constant<int, C::LOADS>;   // stage s+2 may still be in flight
+      wait_vm<2 * C::LOADS>();
+      stage_barrier();
+#pragma unroll
+      for (int r = 0; r < NS; ++r) read_scale(0, r, sa, sb);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) read_frag(0, 0, r, a0, b0);
+      // the stage count is a multiple of four (K % 512 == 0): groups of four stages,
+      // the last group with its tail conditions resolved at compile time
+      int s = 0;
+      for (; s + 4 < nst; s += 4) {
+        step(s, T{}, F{}, WL{}, sa, sb, na, nb);
+        step(s + 1, T{}, T{}, WL{}, na, nb, sa, sb);
+        step(s + 2, T{}, F{}, WL{}, sa, sb, na, nb);
+        step(s + 3, T{}, F{}, WL{}, na, nb, sa, sb);
       }
-    };
-    using T = std::integral_constant<bool, true>;
-    using F = std::integral_constant<bool, false>;
-    using WL = std::integral_constant<int, C::LOADS>;   // stage s+2 may still be in flight
-    issue_scales(0);
-    issue(0);
-    issue(1);
-    issue(2);
-    wait_vm<2 * C::LOADS>();
-    stage_barrier();
-#pragma unroll
-    for (int r = 0; r < NS; ++r) read_scale(0, r, sa, sb);
-#pragma unroll
-    for (int r = 0; r < NR; ++r) read_frag(0, 0, r, a0, b0);
-    // the stage count is a multiple of four (K % 512 == 0): groups of four stages,
-    // the last group with its tail conditions resolved at compile time
-    int s = 0;
-    for (; s + 4 < nst; s += 4) {
       step(s, T{}, F{}, WL{}, sa, sb, na, nb);
-      step(s + 1, T{}, T{}, WL{}, na, nb, sa, sb);
-      step(s + 2, T{}, F{}, WL{}, sa, sb, na, nb);
-      step(s + 3, T{}, F{}, WL{}, na, nb, sa, sb);
-    }
-    step(s, T{}, F{}, WL{}, sa, sb, na, nb);
-    step(s + 1, F{}, F{}, WL{}, na, nb, sa, sb);
-    step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sa, sb, na, nb);
-    step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, na, nb, sa, sb);
-  } else {
-    // bf16 A: the same pipeline as the FP8 path, with k-halves of 64 elements
-    // (block h of each lane half), the weights expanded to bf16 in registers
-    // (one conversion unit = 8 weights of one column, 4 instructions) spread
-    // over the products of the preceding 16-element step
-    uint32_t sb[C::FN], nb[C::FN];
-    v4i bqc[C::FN], bqn[C::FN];            // raw FP4 B of the current / next k-half
-    v8bf afc[4][C::FM], afn[4][C::FM];     // A of the current / next k-half, per 16-element step
-    v8bf bw[C::FN][4];                     // B of the current k-half, expanded
-    auto stage_lds = [&](int s) {
-      return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
-    };
-    // read j of k-half h: j < FN: raw B of column fragment j; then A (step, fm)
-    auto read_frag = [&](int s, int h, int j, v4i (&bq)[C::FN], v8bf (&af)[4][C::FM]) {
-      const uint8_t* la = stage_lds(s);
-      if (j < C::FN) {
-        const int n = wn0 + frag_block(j) * 32 + l32;
-        const int uu = ((n & 1) * 4 + 2 * h + g) ^ xb;
-        bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
-      } else {
-        const int s4 = (j - C::FN) / C::FM, fm = (j - C::FN) % C::FM;
-        const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
-        // bytes 128h + 64g + 16*s4 of the 256-byte stage row: slot 8h + 4g + s4
-        af[s4][fm] = *reinterpret_cast<const v8bf*>(row + (((8 * h + 4 * g + s4) ^ xa) << 4));
-      }
-    };
-    auto read_scale = [&](int s, int j, uint32_t (&tb)[C::FN]) {
-      const uint8_t* lsb = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4) + C::SG_A;
-      tb[j] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + frag_block(j) * 32 + l32) * 16);
-    };
-    // conversion unit (fn, d): the 8 weights of bw[fn][d] (E2M1 x block scale -> bf16, exact)
-    auto expand = [&](int h, int fn, int d, const v4i (&bq)[C::FN], const uint32_t (&tb)[C::FN]) {
-      const float sc = e8m0_to_f32((tb[fn] >> (8 * (2 * h + g))) & 0xff);
-      const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 0);
-      const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 1);
-      const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 2);
-      const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 3);
-      bw[fn][d] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-    };
-    constexpr int MG = C::FN * C::FM;      // products of one 16-element step
-    constexpr int MF = 4 * MG;             // products of one k-half
-    constexpr int NR = C::FN + 4 * C::FM;  // reads of one k-half
-    constexpr int NS = C::FN;              // scale reads of one stage
-    constexpr int R1 = (NR + MF - 1) / MF > 1 ? (NR + MF - 1) / MF : 1;
-    constexpr int R2 = (NR + NS + MF - 1) / MF > 1 ? (NR + NS + MF - 1) / MF : 1;
-    constexpr int D2 = (C::LOADS + MF - 1) / MF;
-    // the products of k-half h from af/bq, with the expansion of step t+1's
-    // weights after the MFMAs of step t (unit fn after the step's product fn*FM),
-    // and EXTRA(i) (reads / DMA) after product i
-    auto half = [&](int h, const v4i (&bq)[C::FN], const v8bf (&af)[4][C::FM], const uint32_t (&tb)[C::FN],
-                    auto&& extra) {
+      step(s + 1, F{}, F{}, WL{}, na, nb, sa, sb);
+      step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sa, sb, na, nb);
+      step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, na, nb, sa, sb);
+    } else {
+      // bf16 A: the same pipeline as the FP8 path, with k-halves of 64 elements
+      // (block h of each lane half), the weights expanded to bf16 in registers
+      // (one conversion unit = 8 weights of one column, 4 instructions) spread
+      // over the products of the preceding 16-element step
+      uint32_t sb[C::FN], nb[C::FN];
+      v4i bqc[C::FN], bqn[C::FN];            // raw FP4 B of the current / next k-half
+      v8bf afc[4][C::FM], afn[4][C::FM];     // A of the current / next k-half, per 16-element step
+      v8bf bw[C::FN][4];                     // B of the current k-half, expanded
+      auto stage_lds = [&](int s) {
+        return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
+      };
+      // read j of k-half h: j < FN: raw B of column fragment j; then A (step, fm)
+      auto read_frag = [&](int s, int h, int j, v4i (&bq)[C::FN], v8bf (&af)[4][C::FM]) {
+        const uint8_t* la = stage_lds(s);
+        if (j < C::FN) {
+          const int n = wn0 + frag_block(j) * 32 + l32;
+          const int uu = ((n & 1) * 4 + 2 * h + g) ^ xb;
+          bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
+        } else {
+          const int s4 = (j - C::FN) / C::FM, fm = (j - C::FN) % C::FM;
+          const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
+          // bytes 128h + 64g + 16*s4 of the 256-byte stage row: slot 8h + 4g + s4
+          af[s4][fm] = *reinterpret_cast<const v8bf*>(row + (((8 * h + 4 * g + s4) ^ xa) << 4));
+        }
+      };
+      auto read_scale = [&](int s, int j, uint32_t (&tb)[C::FN]) {
+        const uint8_t* lsb = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4) + C::SG_A;
+        tb[j] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + frag_block(j) * 32 + l32) * 16);
+      };
+      // conversion unit (fn, d): the 8 weights of bw[fn][d] (E2M1 x block scale -> bf16, exact)
+      auto expand = [&](int h, int fn, int d, const v4i (&bq)[C::FN], const uint32_t (&tb)[C::FN]) {
+        const float sc = e8m0_to_f32((tb[fn] >> (8 * (2 * h + g))) & 0xff);
+        const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 0);
+        const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 1);
+        const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 2);
+        const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 3);
+        bw[fn][d] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+      };
+      constexpr int MG = C::FN * C::FM;      // products of one 16-element step
+      constexpr int MF = 4 * MG;             // products of one k-half
+      constexpr int NR = C::FN + 4 * C::FM;  // reads of one k-half
+      constexpr int NS = C::FN;              // scale reads of one stage
+      constexpr int R1 = (NR + MF - 1) / MF > 1 ? (NR + MF - 1) / MF : 1;
+      constexpr int R2 = (NR + NS + MF - 1) / MF > 1 ? (NR + NS + MF - 1) / MF : 1;
+      constexpr int D2 = (C::LOADS + MF - 1) / MF;
+      // the products of k-half h from af/bq, with the expansion of step t+1's
+      // weights after the MFMAs of step t (unit fn after the step's product fn*FM),
+      // and EXTRA(i) (reads / DMA) after product i
+      auto half = [&](int h, const v4i (&bq)[C::FN], const v8bf (&af)[4][C::FM], const uint32_t (&tb)[C::FN],
+                      auto&& extra) {
 #pragma unroll
-      for (int fn = 0; fn < C::FN; ++fn) expand(h, fn, 0, bq, tb);
+        for (int fn = 0; fn < C::FN; ++fn) expand(h, fn, 0, bq, tb);
 #pragma unroll
-      for (int i = 0; i < MF; ++i) {
-        const int s4 = i / MG, fn = (i % MG) / C::FM, fm = i % C::FM;
-        acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(af[s4][fm], bw[fn][s4], acc[fm][fn], 0, 0, 0);
-        __builtin_amdgcn_sched_barrier(0);
-        if (s4 < 3 && fm == 0) expand(h, fn, s4 + 1, bq, tb);
-        extra(i);
-        __builtin_amdgcn_sched_barrier(0);
-      }
-    };
-    auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&tb)[C::FN], uint32_t (&tnb)[C::FN]) {
-      constexpr bool kIssue = decltype(ISSUE)::value;
-      constexpr bool kScales = decltype(SCALES)::value;
-      constexpr int kWait = decltype(WAIT)::value;
-      half(0, bqc, afc, tb, [&](int i) {
+        for (int i = 0; i < MF; ++i) {
+          const int s4 = i / MG, fn = (i % MG) / C::FM, fm = i % C::FM;
+          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[fn][s4], af[s4][fm], acc[fm][fn], 0, 0, 0);
+          __builtin_amdgcn_sched_barrier(0);
+          if (s4 < 3 && fm == 0) expand(h, fn, s4 + 1, bq, tb);
+          extra(i);
+          __builtin_amdgcn_sched_barrier(0);
+        }
+      };
+      auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&tb)[C::FN], uint32_t (&tnb)[C::FN]) {
+        constexpr bool kIssue = decltype(ISSUE)::value;
+        constexpr bool kScales = decltype(SCALES)::value;
+        constexpr int kWait = decltype(WAIT)::value;
+        half(0, bqc, afc, tb, [&](int i) {
 #pragma unroll
-        for (int r = R1 * i; r < R1 * i + R1; ++r)
-          if (r < NR) read_frag(s, 1, r, bqn, afn);
-      });
+          for (int r = R1 * i; r < R1 * i + R1; ++r)
+            if (r < NR) read_frag(s, 1, r, bqn, afn);
+        });
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+        for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
-      if constexpr (kWait >= 0) {
-        wait_lgkm0();
-        wait_vm<kWait>();
-        stage_barrier();
-      }
-      __builtin_amdgcn_sched_barrier(0);
-      half(1, bqn, afn, tb, [&](int i) {
+          for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
         if constexpr (kWait >= 0) {
-#pragma unroll
-          for (int r = R2 * i; r < R2 * i + R2; ++r) {
-            if (r < NS) read_scale(s + 1, r, tnb);
-            else if (r < NS + NR) read_frag(s + 1, 0, r - NS, bqc, afc);
-          }
+          wait_lgkm0();
+          wait_vm<kWait>();
+          stage_barrier();
         }
-        if constexpr (kIssue) {
+        __builtin_amdgcn_sched_barrier(0);
+        half(1, bqn, afn, tb, [&](int i) {
+          if constexpr (kWait >= 0) {
 #pragma unroll
-          for (int j = D2 * i; j < D2 * i + D2; ++j) {
-            if (j < C::LOADS) issue_one(s + 3, j);
-            if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
+            for (int r = R2 * i; r < R2 * i + R2; ++r) {
+              if (r < NS) read_scale(s + 1, r, tnb);
+              else if (r < NS + NR) read_frag(s + 1, 0, r - NS, bqc, afc);
+            }
           }
-        }
-      });
-    };
-    using T = std::integral_constant<bool, true>;
-    using F = std::integral_constant<bool, false>;
-    using WL = std::integral_constant<int, C::LOADS>;
-    issue_scales(0);
-    issue(0);
-    issue(1);
-    issue(2);
-    wait_vm<2 * C::LOADS>();
-    stage_barrier();
+          if constexpr (kIssue) {
 #pragma unroll
-    for (int r = 0; r < NS; ++r) read_scale(0, r, sb);
+            for (int j = D2 * i; j < D2 * i + D2; ++j) {
+              if (j < C::LOADS) issue_one(s + 3, j);
+              if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
+            }
+          }
+        });
+      };
+      using T = std::integral_constant<bool, true>;
+      using F = std::integral_constant<bool, false>;
+      using WL = std::integral_constant<int, C::LOADS>;
+      wait_vm<2 * C::LOADS>();
+      stage_barrier();
 #pragma unroll
-    for (int r = 0; r < NR; ++r) read_frag(0, 0, r, bqc, afc);
-    int s = 0;
-    for (; s + 4 < nst; s += 4) {
+      for (int r = 0; r < NS; ++r) read_scale(0, r, sb);
+#pragma unroll
+      for (int r = 0; r < NR; ++r) read_frag(0, 0, r, bqc, afc);
+      int s = 0;
+      for (; s + 4 < nst; s += 4) {
+        step(s, T{}, F{}, WL{}, sb, nb);
+        step(s + 1, T{}, T{}, WL{}, nb, sb);
+        step(s + 2, T{}, F{}, WL{}, sb, nb);
+        step(s + 3, T{}, F{}, WL{}, nb, sb);
+      }
       step(s, T{}, F{}, WL{}, sb, nb);
-      step(s + 1, T{}, T{}, WL{}, nb, sb);
-      step(s + 2, T{}, F{}, WL{}, sb, nb);
-      step(s + 3, T{}, F{}, WL{}, nb, sb);
+      step(s + 1, F{}, F{}, WL{}, nb, sb);
+      step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sb, nb);
+      step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, nb, sb);
     }
-    step(s, T{}, F{}, WL{}, sb, nb);
-    step(s + 1, F{}, F{}, WL{}, nb, sb);
-    step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sb, nb);
-    step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, nb, sb);
-  }
 
-  // ---- epilogue: registers -> C in permuted row order ----
-  // gate/up pairing of the SwiGLU layouts: fragment fh holds the gate columns
-  // of 32-column block 2fh, fragment fh + FN/2 the matching up columns of
-  // block 2fh + 1 (see frag_block)
-  {
-  // The epilogue's lane-derived values come from a fresh opaque copy of the
-  // thread index: derived from the one above, its store addresses were
-  // computed ahead of the K loop and kept live through it, which pushed the
-  // eight-wave FC1 tile into spills.
-  asm volatile("v_mov_b32 %0, %1" : "=v"(tid) : "v"(tid_in));
-  const int lane = tid & 63;
-  const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
-  const int wm0 = (wave / C::WAVES_N) * C::WM;
-  const int wn0 = (wave % C::WAVES_N) * C::WN;
-  const int l32 = lane & 31;
-  const int g = lane >> 5;
-  // rows this unit stores (none for a unit run only to keep a block's halves in step)
-  const int srows = store ? mrows : 0;
-  constexpr int HF = C::FN / 2;
-  if constexpr (OUT == MOE_OUT_FP32) {
-    // fp32: straight from the accumulators, one fragment at a time
-    if constexpr (EPI == 0) {
-      // fragment fh holds 32-column block 2fh, fragment fh + FN/2 block 2fh + 1
+
+    // ---- between units ----
+    stage_barrier();   // every wave is done reading the stage and scale buffers
+    const int e_row0 = row0, e_mrows = mrows, e_nt = nt;
+    const int un = __builtin_amdgcn_readfirstlane(next());
+    // the next unit's set-up and first PF stages: issued once the accumulators
+    // are dead (after the last staging write; before a direct epilogue), so that
+    // its offsets need no registers beside them
+    auto prefetch = [&]() {
+      if (EC::EARLY && un >= 0) {
+        setup(un);
+        issue_scales(0);
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
-#pragma unroll
-        for (int fh = 0; fh < HF; ++fh) {
-          const int n = nt * kBN + wn0 + 2 * fh * 32 + l32;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-            float* const crow = static_cast<float*>(p.c) + (size_t)(row0 + r) * p.N;
-            if (r < srows && n < p.N) crow[n] = acc[fm][fh][q];
-            if (r < srows && n + 32 < p.N) crow[n + 32] = acc[fm][fh + HF][q];
+        for (int s = 0; s < EC::PF; ++s) issue(s);
+      }
+    };
+    if constexpr (!EC::STAGED) prefetch();
+
+    // ---- epilogue: registers -> C in permuted row order ----
+    // The products take the weights as their first operand, so each
+    // fragment's accumulator is the transposed 32x32 tile: lane l holds tile
+    // row l % 32 and its accumulator q holds column 8*(q/4) + 4*(l/32) + q%4
+    // of the fragment's 32-column block (four runs of four consecutive
+    // columns; the other four runs sit in the partner lane l ^ 32).  SwiGLU:
+    // fragment fh holds the gate columns of 32-column block 2fh, fragment
+    // fh + FN/2 the matching up columns of block 2fh + 1 (see frag_block), so
+    // gate and up of an output column share a lane and an accumulator index.
+    {
+      // the epilogue's lane-derived values come from a fresh lane index
+      const int lane = lane_id();
+      const int tid = wave * 64 + lane;
+      const int wm0 = (wave / C::WAVES_N) * C::WM;
+      const int wn0 = (wave % C::WAVES_N) * C::WN;
+      const int l32 = lane & 31;
+      const int g = lane >> 5;
+      // rows this unit stores (none for a unit run only to keep a block's halves in step)
+      const int srows = store ? e_mrows : 0;
+      constexpr int HF = C::FN / 2;
+      const int ld = EPI == 0 ? p.N : p.n_out;
+      const int col0 = e_nt * EC::TC;               // the tile's first output column
+      const int ncols = min(EC::TC, ld - col0);     // a multiple of 32 (N and n_out are)
+      if constexpr (!EC::STAGED) {
+        // fp32: each run of four columns straight from the accumulators
+        const bool vec = (reinterpret_cast<uintptr_t>(p.c) & 15) == 0;
+        auto store4 = [&](size_t o, float v0, float v1, float v2, float v3) {
+          float* const d = static_cast<float*>(p.c) + o;
+          if (vec) {
+            *reinterpret_cast<float4*>(d) = make_float4(v0, v1, v2, v3);
+          } else {
+            d[0] = v0; d[1] = v1; d[2] = v2; d[3] = v3;
           }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
-      const int i_base = nt * (kBN / 2) + (wave % C::WAVES_N) * (C::WN / 2);
+        };
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+        for (int fm = 0; fm < C::FM; ++fm) {
+          const int r = wm0 + fm * 32 + l32;
+          const size_t orow = (size_t)(e_row0 + r) * ld;
+          if constexpr (EPI == 0) {
 #pragma unroll
-        for (int fh = 0; fh < HF; ++fh) {
-          const int i = i_base + fh * 32 + l32;
+            for (int f = 0; f < C::FN; ++f) {
+              const int n0 = col0 + wn0 + frag_block(f) * 32;
+              if (r < srows && n0 < ld) {
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-            const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
-            if (r < srows && i < p.n_out) static_cast<float*>(p.c)[(size_t)(row0 + r) * p.n_out + i] = a;
+                for (int j = 0; j < 4; ++j)
+                  store4(orow + n0 + 8 * j + 4 * g, acc[fm][f][4 * j], acc[fm][f][4 * j + 1],
+                         acc[fm][f][4 * j + 2], acc[fm][f][4 * j + 3]);
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
+          } else {
+#pragma unroll
+            for (int fh = 0; fh < HF; ++fh) {
+              const int i0 = col0 + (wave % C::WAVES_N) * (C::WN / 2) + fh * 32;
+              if (r < srows && i0 < ld) {
+#pragma unroll
+                for (int j = 0; j < 4; ++j) {
+                  float a[4];
+#pragma unroll
+                  for (int t = 0; t < 4; ++t) a[t] = silu_mul(acc[fm][fh][4 * j + t], acc[fm][fh + HF][4 * j + t]);
+                  store4(orow + i0 + 8 * j + 4 * g, a[0], a[1], a[2], a[3]);
+                }
+              }
+              __builtin_amdgcn_sched_barrier(0);
+            }
           }
-          __builtin_amdgcn_sched_barrier(0);
         }
-    }
-  } else {
-    // bf16 and MXFP8: the tile goes through LDS (row-major, rows padded by 16
-    // bytes) so that the global stores are whole row segments
-    constexpr bool MX = OUT == MOE_OUT_MXFP8_E4M3;
-    static_assert(!MX || EPI != 0, "MXFP8 output needs the SwiGLU epilogue");
-    constexpr int EB = MX ? 4 : 2;                   // bytes per staged element
-    constexpr int TC = EPI == 0 ? kBN : kBN / 2;    // tile columns
-    constexpr int PITCH = EB * TC + 16;
-    static_assert(BM * PITCH <= C::LDS_TOTAL, "C tile must fit in LDS");
-    stage_barrier();   // every wave is done reading the stage buffers
-    if constexpr (EPI == 0) {
-      // fragment fh holds 32-column block 2fh, fragment fh + FN/2 block 2fh + 1
+      } else {
+        constexpr bool MX = EC::MX;
+        static_assert(!MX || EPI != 0, "MXFP8 output needs the SwiGLU epilogue");
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+        for (int pass = 0; pass < EC::PASSES; ++pass) {
+          const int pr0 = pass * EC::PROWS;   // first tile row of the pass
+          if (wm0 >= pr0 && wm0 < pr0 + EC::PROWS) {   // this wave's rows belong to the pass
 #pragma unroll
-        for (int fh = 0; fh < HF; ++fh) {
-          uint8_t* col = lds + (wn0 + 2 * fh * 32 + l32) * 2;
+            for (int fm = 0; fm < C::FM; ++fm) {
+              uint8_t* const srow = lds + EC::BASE + (wm0 - pr0 + fm * 32 + l32) * EC::PITCH;   // this lane's staged row
+              if constexpr (EPI == 0) {
 #pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-            // v_cvt_pk_bf16_f32 (RNE)
-            *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)acc[fm][fh][q];
-            *reinterpret_cast<__bf16*>(col + 64 + r * PITCH) = (__bf16)acc[fm][fh + HF][q];
+                for (int f = 0; f < C::FN; ++f) {
+                  uint8_t* const d = srow + (wn0 + frag_block(f) * 32 + 4 * g) * 2;
+#pragma unroll
+                  for (int j = 0; j < 4; ++j) {
+                    // v_cvt_pk_bf16_f32 (RNE)
+                    const uint32_t h0 = __builtin_bit_cast(uint16_t, (__bf16)acc[fm][f][4 * j]);
+                    const uint32_t h1 = __builtin_bit_cast(uint16_t, (__bf16)acc[fm][f][4 * j + 1]);
+                    const uint32_t h2 = __builtin_bit_cast(uint16_t, (__bf16)acc[fm][f][4 * j + 2]);
+                    const uint32_t h3 = __builtin_bit_cast(uint16_t, (__bf16)acc[fm][f][4 * j + 3]);
+                    *reinterpret_cast<uint2*>(d + 16 * j) = make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                  }
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              } else {
+#pragma unroll
+                for (int fh = 0; fh < HF; ++fh) {
+                  const int lc = (wave % C::WAVES_N) * (C::WN / 2) + fh * 32;   // the block's first tile column
+                  float a[16];
+#pragma unroll
+                  for (int q = 0; q < 16; ++q) a[q] = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
+                  if constexpr (MX) {
+                    // one 32-element MX block per row: this lane's 16 values and its partner's
+                    float amax = 0.f;
+#pragma unroll
+                    for (int q = 0; q < 16; ++q) amax = fmaxf(amax, fabsf(a[q]));
+                    amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+                    const int x = mxfp8_block_exp(amax);
+#pragma unroll
+                    for (int j = 0; j < 4; ++j)
+                      *reinterpret_cast<uint32_t*>(srow + lc + 8 * j + 4 * g) =
+                          e4m3x4_rne(ldexpf(a[4 * j], -x), ldexpf(a[4 * j + 1], -x), ldexpf(a[4 * j + 2], -x),
+                                     ldexpf(a[4 * j + 3], -x));
+                    if (g == 0) lds[EC::BASE + EC::SC_OFF + (wm0 - pr0 + fm * 32 + l32) * (EC::TC / 32) + lc / 32] = (uint8_t)(x + 127);
+                  } else {
+#pragma unroll
+                    for (int j = 0; j < 4; ++j) {
+                      const uint32_t h0 = __builtin_bit_cast(uint16_t, (__bf16)a[4 * j]);
+                      const uint32_t h1 = __builtin_bit_cast(uint16_t, (__bf16)a[4 * j + 1]);
+                      const uint32_t h2 = __builtin_bit_cast(uint16_t, (__bf16)a[4 * j + 2]);
+                      const uint32_t h3 = __builtin_bit_cast(uint16_t, (__bf16)a[4 * j + 3]);
+                      *reinterpret_cast<uint2*>(srow + (lc + 8 * j + 4 * g) * 2) =
+                          make_uint2(h0 | (h1 << 16), h2 | (h3 << 16));
+                    }
+                  }
+                  __builtin_amdgcn_sched_barrier(0);
+                }
+              }
+            }
           }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    } else {
+          if (pass == EC::PASSES - 1) prefetch();
+          stage_barrier();
+          // The pass's rows -> C in whole row segments, 16 bytes a thread.  The
+          // staging is read with lds_read16/lds_read4 (see there): a plain LDS
+          // read here would be ordered after the next unit's DMA just issued.
+          const int prows = min(EC::PROWS, srows - pr0);   // may be <= 0
+          constexpr int CB = MX ? 16 : 8;                  // elements per 16-byte chunk
+          constexpr int CPR = EC::TC / CB;                 // chunks per staged row
+          const uint32_t sbase = lds_addr(lds) + EC::BASE;
+          if constexpr (!MX) {
+            const bool vec = ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && (ld % 8 == 0);
+            uint16_t* const out = static_cast<uint16_t*>(p.c) + (size_t)(e_row0 + pr0) * ld + col0;
+            for (int idx = tid; idx < prows * CPR; idx += C::NT) {
+              const int r = idx / CPR, c = (idx % CPR) * CB;
+              if (c >= ncols) continue;
+              const uint4 v = lds_read16(sbase + r * EC::PITCH + c * 2);
+              uint16_t* dst = out + (size_t)r * ld + c;
+              if (vec) {
+                *reinterpret_cast<uint4*>(dst) = v;
+              } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-      for (int fm = 0; fm < C::FM; ++fm)
+                for (int j = 0; j < 8; ++j) dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+              }
+            }
+          } else {
+            const bool vec = (reinterpret_cast<uintptr_t>(p.c) & 15) == 0;   // ld % 32 == 0 (the host checks)
+            uint8_t* const out = static_cast<uint8_t*>(p.c) + (size_t)(e_row0 + pr0) * ld + col0;
+            for (int idx = tid; idx < prows * CPR; idx += C::NT) {
+              const int r = idx / CPR, c = (idx % CPR) * CB;
+              if (c >= ncols) continue;
+              const uint4 v = lds_read16(sbase + r * EC::PITCH + c);
+              uint8_t* dst = out + (size_t)r * ld + c;
+              if (vec) {
+                *reinterpret_cast<uint4*>(dst) = v;
+              } else {
+                const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
-        for (int fh = 0; fh < HF; ++fh) {
-          uint8_t* col = lds + ((wave % C::WAVES_N) * (C::WN / 2) + fh * 32 + l32) * EB;
-#pragma unroll
-          for (int q = 0; q < 16; ++q) {
-            const int r = wm0 + fm * 32 + 8 * (q >> 2) + 4 * g + (q & 3);
-            const float a = silu_mul(acc[fm][fh][q], acc[fm][fh + HF][q]);
-            if constexpr (MX) *reinterpret_cast<float*>(col + r * PITCH) = a;
-            else *reinterpret_cast<__bf16*>(col + r * PITCH) = (__bf16)a;
+                for (int j = 0; j < 16; ++j) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
+              }
+            }
+            // the rows' E8M0 bytes: TC / 32 = 4 consecutive bytes per row
+            static_assert(EC::TC / 32 == 4, "one 4-byte word of scales per staged row");
+            const int sld = ld / 32;
+            const bool svec = (reinterpret_cast<uintptr_t>(p.c_scales) & 3) == 0 && sld % 4 == 0 && ncols == EC::TC;
+            for (int idx = tid; idx < prows; idx += C::NT) {
+              const uint32_t w = lds_read4(sbase + EC::SC_OFF + idx * 4);
+              uint8_t* const osc = p.c_scales + (size_t)(e_row0 + pr0 + idx) * sld + col0 / 32;
+              if (svec) {
+                *reinterpret_cast<uint32_t*>(osc) = w;
+              } else {
+                for (int b = 0; b < ncols / 32; ++b) osc[b] = (uint8_t)(w >> (8 * b));
+              }
+            }
           }
-          __builtin_amdgcn_sched_barrier(0);
-        }
-    }
-    stage_barrier();
-    const int ld = EPI == 0 ? p.N : p.n_out;
-    const int col0 = nt * TC;
-    const int ncols = min(TC, ld - col0);
-    if constexpr (!MX) {
-      const bool vec = ((reinterpret_cast<uintptr_t>(p.c) & 15) == 0) && (ld % 8 == 0);
-      constexpr int CPR = TC / 8;   // 16-byte chunks per tile row
-      uint16_t* const out = static_cast<uint16_t*>(p.c) + (size_t)row0 * ld + col0;
-      for (int idx = tid; idx < srows * CPR; idx += C::NT) {
-        const int r = idx / CPR, c = (idx % CPR) * 8;
-        if (c >= ncols) continue;
-        const uint4 v = *reinterpret_cast<const uint4*>(lds + r * PITCH + c * 2);
-        uint16_t* dst = out + (size_t)r * ld + c;
-        if (vec && c + 8 <= ncols) {
-          *reinterpret_cast<uint4*>(dst) = v;
-        } else {
-          const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-#pragma unroll
-          for (int j = 0; j < 8; ++j)
-            if (c + j < ncols) dst[j] = (uint16_t)(w[j >> 1] >> (16 * (j & 1)));
+          stage_barrier();   // the staging is read before anything writes it again
         }
       }
-    } else {
-      // one 32-element MX block per thread and step: amax -> E8M0 exponent X ->
-      // E4M3 codes of v * 2^-X; ld is a multiple of 32 (the host checks)
-      const bool vec = (reinterpret_cast<uintptr_t>(p.c) & 15) == 0 && ld % 16 == 0;
-      constexpr int BPR = TC / 32;   // blocks per tile row
-      uint8_t* const out = static_cast<uint8_t*>(p.c) + (size_t)row0 * ld + col0;
-      uint8_t* const osc = p.c_scales + (size_t)row0 * (ld / 32) + col0 / 32;
-      for (int idx = tid; idx < srows * BPR; idx += C::NT) {
-        const int r = idx / BPR, c = (idx % BPR) * 32;
-        if (c >= ncols) continue;
-        const float4* src = reinterpret_cast<const float4*>(lds + r * PITCH + c * 4);
-        float v[32];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-          const float4 f = src[j];
-          v[4 * j] = f.x; v[4 * j + 1] = f.y; v[4 * j + 2] = f.z; v[4 * j + 3] = f.w;
-        }
-        float amax = 0.f;
-#pragma unroll
-        for (int j = 0; j < 32; ++j) amax = fmaxf(amax, fabsf(v[j]));
-        const int x = mxfp8_block_exp(amax);
-        uint32_t w[8];
-#pragma unroll
-        for (int j = 0; j < 8; ++j)
-          w[j] = e4m3x4_rne(ldexpf(v[4 * j], -x), ldexpf(v[4 * j + 1], -x),
-                            ldexpf(v[4 * j + 2], -x), ldexpf(v[4 * j + 3], -x));
-        uint8_t* dst = out + (size_t)r * ld + c;
-        if (vec) {
-          reinterpret_cast<uint4*>(dst)[0] = make_uint4(w[0], w[1], w[2], w[3]);
-          reinterpret_cast<uint4*>(dst)[1] = make_uint4(w[4], w[5], w[6], w[7]);
-        } else {
-#pragma unroll
-          for (int j = 0; j < 32; ++j) dst[j] = (uint8_t)(w[j >> 2] >> (8 * (j & 3)));
-        }
-        osc[(size_t)r * (ld / 32) + c / 32] = (uint8_t)(x + 127);
-      }
     }
-  }
+    settle();
+    if (un < 0) break;
+    if constexpr (!EC::EARLY) {
+      setup(un);
+      issue_scales(0);
+    }
+    // the next unit's stages that the staging's buffers hold (all of them
+    // without the early start)
+#pragma unroll
+    for (int s = EC::EARLY ? EC::PF : 0; s < C::NST; ++s) issue(s);
   }
 }
 
@@ -1098,24 +1241,32 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
   const int u_end = min(units, u_first + per_xcd);
 
   // Units of an XCD's range are handed out dynamically (blocks whose units
-  // end early take more; blocks that start late take fewer).  Thread
-  // 0 draws the next index with an atomic one unit ahead; the index reaches
-  // the other threads through a slot in scale buffer 1, which is idle between
-  // units.
+  // end early take more; blocks that start late take fewer).  Thread 0 draws
+  // the next index with an atomic one unit ahead; the index reaches the other
+  // threads through a slot in scale buffer 1, which is idle between a unit's
+  // last products and the next unit's second stage.
   int* const unit_slot = reinterpret_cast<int*>(lds + C::NST * C::LDS_STAGE + C::LDS_SG);
   if (threadIdx.x == 0) *unit_slot = atomicAdd(&p.unit_ctr[xcd], 1);
   stage_barrier();
-  int u = u_first + *unit_slot;
-  while (u < u_end) {
-    int u_next = 0;
-    if (threadIdx.x == 0) u_next = atomicAdd(&p.unit_ctr[xcd], 1);
-    run_unit<BM, FP8, EPI, OUT, TILED, C::NW>(p, u, count, threadIdx.x, lds, true);
-    // every wave is done with LDS before the next unit refills it
+  const int u = u_first + *unit_slot;
+  if (u >= u_end) return;   // the same in every thread
+  // Thread 0's draw of the unit after the current one, in a scalar register
+  // (wave 0's first lane is thread 0).  next() publishes it and issues the
+  // following draw; settle() takes that draw's result after the epilogue, so
+  // that the atomic's latency passes under it.
+  int d = 0;
+  if (threadIdx.x == 0) d = atomicAdd(&p.unit_ctr[xcd], 1);
+  int drawn = __builtin_amdgcn_readfirstlane(d);
+  auto next = [&]() -> int {
+    if (threadIdx.x == 0) *unit_slot = drawn;
     stage_barrier();
-    if (threadIdx.x == 0) *unit_slot = u_next;
-    stage_barrier();
-    u = u_first + *unit_slot;
-  }
+    const int n = u_first + *unit_slot;
+    d = 0;
+    if (threadIdx.x == 0 && n < u_end) d = atomicAdd(&p.unit_ctr[xcd], 1);
+    return n < u_end ? n : -1;
+  };
+  auto settle = [&]() { drawn = __builtin_amdgcn_readfirstlane(d); };
+  run_units<BM, FP8, EPI, OUT, TILED, C::NW>(p, u, count, threadIdx.x, lds, true, next, settle);
 }
 
 // ---- every row-tile class of a call in one launch ------------------------
@@ -1145,9 +1296,9 @@ __global__ __launch_bounds__(512) void gemm_mixed_kernel(Params p, int small_cus
   using CF = Cfg2<256, FP8, 8>;
   using CS = Cfg2<32, FP8, 4>;
   static_assert(CS::LDS_TOTAL <= kSmallHalfLds, "a <= 32-row unit fits half the LDS");
-  constexpr int kSlots = CF::NST * CF::LDS_STAGE + CF::LDS_SG;   // idle between units
+  constexpr int kSlots = CF::NST * CF::LDS_STAGE + CF::LDS_SG;   // scale buffer 1 of the 256-row units
   static_assert(kSmallHalfLds + CS::LDS_TOTAL <= kSlots && Cfg2<128, FP8, 8>::LDS_TOTAL <= kSlots,
-                "the draw slots lie beyond every unit's LDS");
+                "the draw slots lie beyond the LDS of every unit but the 256-row ones");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::LDS_TOTAL];
   int* const slot = reinterpret_cast<int*>(lds + kSlots);   // this block's next draw, per half
 
@@ -1157,47 +1308,69 @@ __global__ __launch_bounds__(512) void gemm_mixed_kernel(Params p, int small_cus
   const Tile* const lists = p.tiles;
   const int32_t* const counts = p.tile_count;
   int32_t* const ctr = p.unit_ctr;
+  auto none = []() -> int { return -1; };
 
   int ph = 0;          // position in this block's queue order
-  bool have = false;   // the slots already hold the next draws from the current queue
+  bool have = false;   // <= 32-row queue: the slots already hold the next draws
   while (ph < kClasses) {
     const int c = small_first ? ph : kClasses - 1 - ph;   // row-tile class of the current queue
-    const bool dual = c == 0;
     const int cnt = counts[c];
     const int units = cnt * p.n_tiles;
     const int per_xcd = (units + kXcds - 1) / kXcds;
     const int u0 = xcd * per_xcd, u1 = min(units, u0 + per_xcd);
     int32_t* const uc = ctr + c * kXcds + xcd;
-    // the threads that draw: thread 0 (a single unit) or the first of each half
-    const bool drawer = dual ? (threadIdx.x & 255) == 0 : threadIdx.x == 0;
-    if (!have && drawer) slot[half] = atomicAdd(uc, 1);
-    stage_barrier();
-    const int a = u0 + slot[0], b = u0 + slot[1];
-    stage_barrier();   // both slots read before either is written again
-    const bool va = a < u1, vb = dual && b < u1;
-    if (!va && !vb) {
-      ++ph;
-      have = false;
-      continue;
-    }
-    int nxt = 0;
-    if (drawer) nxt = atomicAdd(uc, 1);   // one unit ahead
     Params q = p;
     q.tiles = lists + c * p.tile_cap;
-    if (c == 3) {
-      run_unit<256, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true);
-    } else if (c == 2) {
-      run_unit<128, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true);
-    } else if (c == 1) {
-      run_unit<64, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true);
-    } else {
+    if (c == 0) {
+      // two units side by side, one per half, each drawn by the half's first thread
+      const bool drawer = (threadIdx.x & 255) == 0;
+      if (!have && drawer) slot[half] = atomicAdd(uc, 1);
+      stage_barrier();
+      const int a = u0 + slot[0], b = u0 + slot[1];
+      stage_barrier();   // both slots read before either is written again
+      const bool va = a < u1, vb = b < u1;
+      if (!va && !vb) {
+        ++ph;
+        have = false;
+        continue;
+      }
+      int nxt = 0;
+      if (drawer) nxt = atomicAdd(uc, 1);   // one unit ahead
       const bool mine = half ? vb : va;
       const int u = (half ? vb : !va) ? b : a;   // a half without a unit runs its partner's
-      run_unit<32, FP8, EPI, OUT, true, 4>(q, u, cnt, threadIdx.x & 255, lds + half * kSmallHalfLds, mine);
+      run_units<32, FP8, EPI, OUT, true, 4>(q, u, cnt, threadIdx.x & 255, lds + half * kSmallHalfLds, mine, none,
+                                            [] {});
+      stage_barrier();   // every wave is done with the LDS
+      if (drawer) slot[half] = nxt;
+      have = true;
+      continue;
     }
-    stage_barrier();   // every wave is done with the LDS
-    if (drawer) slot[half] = nxt;
-    have = true;
+    // one unit stream for the whole block, the next unit's first stages under each epilogue
+    if (threadIdx.x == 0) slot[0] = atomicAdd(uc, 1);
+    stage_barrier();
+    const int a = u0 + slot[0];
+    stage_barrier();   // the slot is read before it is written again
+    if (a < u1) {
+      // thread 0's draws, one unit ahead, as in gemm_dma_kernel
+      int d = 0;
+      if (threadIdx.x == 0) d = atomicAdd(uc, 1);
+      int drawn = __builtin_amdgcn_readfirstlane(d);
+      auto next = [&]() -> int {
+        if (threadIdx.x == 0) slot[0] = drawn;
+        stage_barrier();
+        const int n = u0 + slot[0];
+        d = 0;
+        if (threadIdx.x == 0 && n < u1) d = atomicAdd(uc, 1);
+        return n < u1 ? n : -1;
+      };
+      auto settle = [&]() { drawn = __builtin_amdgcn_readfirstlane(d); };
+      if (c == 3) run_units<256, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true, next, settle);
+      else if (c == 2) run_units<128, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true, next, settle);
+      else run_units<64, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true, next, settle);
+      stage_barrier();   // every wave is done with the LDS and the slot
+    }
+    have = false;
+    ++ph;
   }
 }
 
