@@ -893,121 +893,133 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
       // bf16 A: the same pipeline as the FP8 path, with k-halves of 64 elements
       // (block h of each lane half), the weights expanded to bf16 in registers
       // (one conversion unit = 8 weights of one column, 4 instructions) spread
-      // over the products of the preceding 16-element step
-      uint32_t sb[C::FN], nb[C::FN];
-      v4i bqc[C::FN], bqn[C::FN];            // raw FP4 B of the current / next k-half
-      v8bf afc[4][C::FM], afn[4][C::FM];     // A of the current / next k-half, per 16-element step
-      v8bf bw[C::FN][4];                     // B of the current k-half, expanded
-      auto stage_lds = [&](int s) {
-        return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
-      };
-      // read j of k-half h: j < FN: raw B of column fragment j; then A (step, fm)
-      auto read_frag = [&](int s, int h, int j, v4i (&bq)[C::FN], v8bf (&af)[4][C::FM]) {
-        const uint8_t* la = stage_lds(s);
-        if (j < C::FN) {
-          const int n = wn0 + frag_block(j) * 32 + l32;
-          const int uu = ((n & 1) * 4 + 2 * h + g) ^ xb;
-          bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
-        } else {
-          const int s4 = (j - C::FN) / C::FM, fm = (j - C::FN) % C::FM;
-          const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
-          // bytes 128h + 64g + 16*s4 of the 256-byte stage row: slot 8h + 4g + s4
-          af[s4][fm] = *reinterpret_cast<const v8bf*>(row + (((8 * h + 4 * g + s4) ^ xa) << 4));
-        }
-      };
-      auto read_scale = [&](int s, int j, uint32_t (&tb)[C::FN]) {
-        const uint8_t* lsb = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4) + C::SG_A;
-        tb[j] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + frag_block(j) * 32 + l32) * 16);
-      };
-      // conversion unit (fn, d): the 8 weights of bw[fn][d] (E2M1 x block scale -> bf16, exact)
-      auto expand = [&](int h, int fn, int d, const v4i (&bq)[C::FN], const uint32_t (&tb)[C::FN]) {
-        const float sc = e8m0_to_f32((tb[fn] >> (8 * (2 * h + g))) & 0xff);
-        const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 0);
-        const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 1);
-        const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 2);
-        const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 3);
-        bw[fn][d] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      };
-      constexpr int MG = C::FN * C::FM;      // products of one 16-element step
-      constexpr int MF = 4 * MG;             // products of one k-half
-      constexpr int NR = C::FN + 4 * C::FM;  // reads of one k-half
-      constexpr int NS = C::FN;              // scale reads of one stage
-      constexpr int R1 = (NR + MF - 1) / MF > 1 ? (NR + MF - 1) / MF : 1;
-      constexpr int R2 = (NR + NS + MF - 1) / MF > 1 ? (NR + NS + MF - 1) / MF : 1;
-      constexpr int D2 = (C::LOADS + MF - 1) / MF;
-      // the products of k-half h from af/bq, with the expansion of step t+1's
-      // weights after the MFMAs of step t (unit fn after the step's product fn*FM),
-      // and EXTRA(i) (reads / DMA) after product i
-      auto half = [&](int h, const v4i (&bq)[C::FN], const v8bf (&af)[4][C::FM], const uint32_t (&tb)[C::FN],
-                      auto&& extra) {
+      // over the products of the preceding 16-element step.  FMA: the 32-row
+      // fragments the unit's rows reach; the others' products and A reads are
+      // left out (their accumulators stay zero and their rows are not stored).
+      auto bf16_kloop = [&](auto fma_c) {
+        constexpr int FMA = decltype(fma_c)::value;
+        uint32_t sb[C::FN], nb[C::FN];
+        v4i bqc[C::FN], bqn[C::FN];            // raw FP4 B of the current / next k-half
+        v8bf afc[4][FMA], afn[4][FMA];         // A of the current / next k-half, per 16-element step
+        v8bf bw[C::FN][4];                     // B of the current k-half, expanded
+        auto stage_lds = [&](int s) {
+          return lds + __builtin_amdgcn_readfirstlane((s % C::NST) * C::LDS_STAGE);
+        };
+        // read j of k-half h: j < FN: raw B of column fragment j; then A (step, fm)
+        auto read_frag = [&](int s, int h, int j, v4i (&bq)[C::FN], v8bf (&af)[4][FMA]) {
+          const uint8_t* la = stage_lds(s);
+          if (j < C::FN) {
+            const int n = wn0 + frag_block(j) * 32 + l32;
+            const int uu = ((n & 1) * 4 + 2 * h + g) ^ xb;
+            bq[j] = *reinterpret_cast<const v4i*>(la + C::LDS_A + (n >> 1) * 128 + (uu << 4));
+          } else {
+            const int s4 = (j - C::FN) / FMA, fm = (j - C::FN) % FMA;
+            const uint8_t* row = la + (wm0 + fm * 32 + l32) * C::RA;
+            // bytes 128h + 64g + 16*s4 of the 256-byte stage row: slot 8h + 4g + s4
+            af[s4][fm] = *reinterpret_cast<const v8bf*>(row + (((8 * h + 4 * g + s4) ^ xa) << 4));
+          }
+        };
+        auto read_scale = [&](int s, int j, uint32_t (&tb)[C::FN]) {
+          const uint8_t* lsb = sg + __builtin_amdgcn_readfirstlane(((s >> 2) & 1) * C::LDS_SG + (s & 3) * 4) + C::SG_A;
+          tb[j] = *reinterpret_cast<const uint32_t*>(lsb + (wn0 + frag_block(j) * 32 + l32) * 16);
+        };
+        // conversion unit (fn, d): the 8 weights of bw[fn][d] (E2M1 x block scale -> bf16, exact)
+        auto expand = [&](int h, int fn, int d, const v4i (&bq)[C::FN], const uint32_t (&tb)[C::FN]) {
+          const float sc = e8m0_to_f32((tb[fn] >> (8 * (2 * h + g))) & 0xff);
+          const v2bf p0 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 0);
+          const v2bf p1 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 1);
+          const v2bf p2 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 2);
+          const v2bf p3 = __builtin_amdgcn_cvt_scalef32_pk_bf16_fp4((uint32_t)bq[fn][d], sc, 3);
+          bw[fn][d] = v8bf{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+        };
+        constexpr int MG = C::FN * FMA;        // products of one 16-element step
+        constexpr int MF = 4 * MG;             // products of one k-half
+        constexpr int NR = C::FN + 4 * FMA;    // reads of one k-half
+        constexpr int NS = C::FN;              // scale reads of one stage
+        constexpr int R1 = (NR + MF - 1) / MF > 1 ? (NR + MF - 1) / MF : 1;
+        constexpr int R2 = (NR + NS + MF - 1) / MF > 1 ? (NR + NS + MF - 1) / MF : 1;
+        constexpr int D2 = (C::LOADS + MF - 1) / MF;
+        // the products of k-half h from af/bq, with the expansion of step t+1's
+        // weights after the MFMAs of step t (unit fn after the step's product fn*FM),
+        // and EXTRA(i) (reads / DMA) after product i
+        auto half = [&](int h, const v4i (&bq)[C::FN], const v8bf (&af)[4][FMA], const uint32_t (&tb)[C::FN],
+                        auto&& extra) {
 #pragma unroll
-        for (int fn = 0; fn < C::FN; ++fn) expand(h, fn, 0, bq, tb);
+          for (int fn = 0; fn < C::FN; ++fn) expand(h, fn, 0, bq, tb);
 #pragma unroll
-        for (int i = 0; i < MF; ++i) {
-          const int s4 = i / MG, fn = (i % MG) / C::FM, fm = i % C::FM;
-          acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[fn][s4], af[s4][fm], acc[fm][fn], 0, 0, 0);
-          __builtin_amdgcn_sched_barrier(0);
-          if (s4 < 3 && fm == 0) expand(h, fn, s4 + 1, bq, tb);
-          extra(i);
-          __builtin_amdgcn_sched_barrier(0);
-        }
-      };
-      auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&tb)[C::FN], uint32_t (&tnb)[C::FN]) {
-        constexpr bool kIssue = decltype(ISSUE)::value;
-        constexpr bool kScales = decltype(SCALES)::value;
-        constexpr int kWait = decltype(WAIT)::value;
-        half(0, bqc, afc, tb, [&](int i) {
+          for (int i = 0; i < MF; ++i) {
+            const int s4 = i / MG, fn = (i % MG) / FMA, fm = i % FMA;
+            acc[fm][fn] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(bw[fn][s4], af[s4][fm], acc[fm][fn], 0, 0, 0);
+            __builtin_amdgcn_sched_barrier(0);
+            if (s4 < 3 && fm == 0) expand(h, fn, s4 + 1, bq, tb);
+            extra(i);
+            __builtin_amdgcn_sched_barrier(0);
+          }
+        };
+        auto step = [&](int s, auto ISSUE, auto SCALES, auto WAIT, uint32_t (&tb)[C::FN], uint32_t (&tnb)[C::FN]) {
+          constexpr bool kIssue = decltype(ISSUE)::value;
+          constexpr bool kScales = decltype(SCALES)::value;
+          constexpr int kWait = decltype(WAIT)::value;
+          half(0, bqc, afc, tb, [&](int i) {
 #pragma unroll
-          for (int r = R1 * i; r < R1 * i + R1; ++r)
-            if (r < NR) read_frag(s, 1, r, bqn, afn);
-        });
+            for (int r = R1 * i; r < R1 * i + R1; ++r)
+              if (r < NR) read_frag(s, 1, r, bqn, afn);
+          });
 #pragma unroll
-        for (int fm = 0; fm < C::FM; ++fm)
+          for (int fm = 0; fm < C::FM; ++fm)
 #pragma unroll
-          for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
-        if constexpr (kWait >= 0) {
-          wait_lgkm0();
-          wait_vm<kWait>();
-          stage_barrier();
-        }
-        __builtin_amdgcn_sched_barrier(0);
-        half(1, bqn, afn, tb, [&](int i) {
+            for (int fn = 0; fn < C::FN; ++fn) asm volatile("" : "+a"(acc[fm][fn]));
           if constexpr (kWait >= 0) {
-#pragma unroll
-            for (int r = R2 * i; r < R2 * i + R2; ++r) {
-              if (r < NS) read_scale(s + 1, r, tnb);
-              else if (r < NS + NR) read_frag(s + 1, 0, r - NS, bqc, afc);
-            }
+            wait_lgkm0();
+            wait_vm<kWait>();
+            stage_barrier();
           }
-          if constexpr (kIssue) {
+          __builtin_amdgcn_sched_barrier(0);
+          half(1, bqn, afn, tb, [&](int i) {
+            if constexpr (kWait >= 0) {
 #pragma unroll
-            for (int j = D2 * i; j < D2 * i + D2; ++j) {
-              if (j < C::LOADS) issue_one(s + 3, j);
-              if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
+              for (int r = R2 * i; r < R2 * i + R2; ++r) {
+                if (r < NS) read_scale(s + 1, r, tnb);
+                else if (r < NS + NR) read_frag(s + 1, 0, r - NS, bqc, afc);
+              }
             }
-          }
-        });
-      };
-      using T = std::integral_constant<bool, true>;
-      using F = std::integral_constant<bool, false>;
-      using WL = std::integral_constant<int, C::LOADS>;
-      wait_vm<2 * C::LOADS>();
-      stage_barrier();
+            if constexpr (kIssue) {
 #pragma unroll
-      for (int r = 0; r < NS; ++r) read_scale(0, r, sb);
+              for (int j = D2 * i; j < D2 * i + D2; ++j) {
+                if (j < C::LOADS) issue_one(s + 3, j);
+                if (kScales && j == C::LOADS - 1) issue_scales((s + 3) >> 2);
+              }
+            }
+          });
+        };
+        using T = std::integral_constant<bool, true>;
+        using F = std::integral_constant<bool, false>;
+        using WL = std::integral_constant<int, C::LOADS>;
+        wait_vm<2 * C::LOADS>();
+        stage_barrier();
 #pragma unroll
-      for (int r = 0; r < NR; ++r) read_frag(0, 0, r, bqc, afc);
-      int s = 0;
-      for (; s + 4 < nst; s += 4) {
+        for (int r = 0; r < NS; ++r) read_scale(0, r, sb);
+#pragma unroll
+        for (int r = 0; r < NR; ++r) read_frag(0, 0, r, bqc, afc);
+        int s = 0;
+        for (; s + 4 < nst; s += 4) {
+          step(s, T{}, F{}, WL{}, sb, nb);
+          step(s + 1, T{}, T{}, WL{}, nb, sb);
+          step(s + 2, T{}, F{}, WL{}, sb, nb);
+          step(s + 3, T{}, F{}, WL{}, nb, sb);
+        }
         step(s, T{}, F{}, WL{}, sb, nb);
-        step(s + 1, T{}, T{}, WL{}, nb, sb);
-        step(s + 2, T{}, F{}, WL{}, sb, nb);
-        step(s + 3, T{}, F{}, WL{}, nb, sb);
+        step(s + 1, F{}, F{}, WL{}, nb, sb);
+        step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sb, nb);
+        step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, nb, sb);
+      };
+      if constexpr (C::WAVES_M == 1 && C::FM == 4) {
+        // the full 128-row tile: a unit of at most 96 rows leaves its last fragment empty
+        if (mrows > 96) bf16_kloop(std::integral_constant<int, 4>{});
+        else bf16_kloop(std::integral_constant<int, 3>{});
+      } else {
+        bf16_kloop(std::integral_constant<int, C::FM>{});
       }
-      step(s, T{}, F{}, WL{}, sb, nb);
-      step(s + 1, F{}, F{}, WL{}, nb, sb);
-      step(s + 2, F{}, F{}, std::integral_constant<int, 0>{}, sb, nb);
-      step(s + 3, F{}, F{}, std::integral_constant<int, -1>{}, nb, sb);
     }
 
 

@@ -118,7 +118,9 @@ def _offsets(counts):
 # one to five groups of four stages
 @pytest.mark.parametrize("K", [160, 512, 1024, 1536, 2560])
 @pytest.mark.parametrize("fp8", [False, True])
-@pytest.mark.parametrize("counts", [[40, 0, 300], [1, 33, 64, 65, 129, 256, 257]])
+# [96, 97, 200, 72]: the bf16 128-row tile on either side of the 96 rows up to
+# which it leaves its last 32-row fragment out (200 = a full tile + 72)
+@pytest.mark.parametrize("counts", [[40, 0, 300], [1, 33, 64, 65, 129, 256, 257], [96, 97, 200, 72]])
 def test_gemm_one_hot_rows_return_the_dequantised_weights_bitwise(fp8, counts, K):
     """A row r of expert e is the unit vector on column (r - off[e]) % K, so
     C[r][n] = dequant(W_e)[n][(r - off[e]) % K] exactly (one nonzero product)."""
