@@ -43,6 +43,7 @@
 // the activations as the second, accumulate the transposed tile: lane l owns
 // one output row, which makes the per-row MX block amax of the MXFP8 epilogue
 // one exchange with the partner lane l ^ 32.
+#include <algorithm>
 #include <type_traits>
 
 #include "internal.h"
@@ -81,6 +82,7 @@ struct Params {
   int32_t* unit_ctr;          // [8] per-XCD unit counters of this launch (zeroed by the planner)
   int tile_cap;               // the mixed launch: stride between the classes' tile lists
   int a_gather_div;
+  uint32_t a_bytes, as_bytes;  // gathered A: bytes of A and of its scales from their starts (< 2^32)
   int N, K, n_out, n_tiles;
   int layout;  // 0 none, 1 split, 2 interleaved
 };
@@ -442,12 +444,14 @@ __device__ __forceinline__ int a_swz(int r) {
 }
 __device__ __forceinline__ int b_swz(int line) { return ((line >> 1) & 3) ^ ((line & 1) << 1); }
 
-// Raw buffer resource over [base, base + 4 GiB).  The DMA below addresses
-// with a 32-bit per-lane offset plus a uniform (scalar) stage offset, which
-// keeps one VGPR per load stream and no 64-bit address arithmetic in the
-// loop; the host bounds every offset below 2^32.
-__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base) {
-  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)0xffffffff, 0x00020000);
+// Raw buffer resource over [base, base + bytes) (4 GiB by default).  The DMA
+// below addresses with a 32-bit per-lane offset plus a uniform (scalar) stage
+// offset, which keeps one VGPR per load stream and no 64-bit address
+// arithmetic in the loop; the host bounds every offset below 2^32.  A load
+// at an offset past `bytes` is out of the resource's range: it returns zeros
+// without a memory request (the tiles' padding rows use that).
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void* base, uint32_t bytes = 0xffffffffu) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes, 0x00020000);
 }
 
 // 16 bytes per lane, global -> LDS (lane i writes dst + 16 i)
@@ -644,9 +648,16 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
     const size_t w_expert = (size_t)e * p.N;
 
     // DMA sources: uniform bases, 32-bit per-lane byte offsets (stage 0).
-    // Gathered A rows: offsets from the start of A; contiguous A rows: from the tile's first row.
+    // Gathered A rows: offsets from the start of A; contiguous A rows: from the
+    // tile's first row.  In tiles of up to 64 rows the rows past the tile's
+    // last one (most of a decode tile's 32 rows) load from the end of the A
+    // resource's range, which reads zeros and moves no data; larger tiles
+    // repeat their last row (rarely padded, and their K loop has no register
+    // to spare for the range).
+    constexpr bool kPadZero = BM <= 64;
     const bool gather = p.a_gather != nullptr;
     const uint8_t* const a_base = gather ? p.a : p.a + (size_t)row0 * a_row_bytes;
+    const uint32_t a_nrec = !kPadZero ? 0xffffffffu : gather ? p.a_bytes : (uint32_t)mrows * (uint32_t)a_row_bytes;
     {
       int arow[C::A_I];
 #pragma unroll
@@ -663,7 +674,7 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
       for (int i = 0; i < C::A_I; ++i) {
         const int r = (wave * C::A_I + i) * C::A_ROWS_PER_I + lane / C::SA;
         const int chunk = (lane % C::SA) ^ a_swz<FP8>(r);
-        a_off[i] = (uint32_t)arow[i] * (uint32_t)a_row_bytes + chunk * 16;
+        a_off[i] = (!kPadZero || r < mrows) ? (uint32_t)arow[i] * (uint32_t)a_row_bytes + chunk * 16 : a_nrec;
       }
     }
     // B: canonical weights are addressed row by row (tile column j of the
@@ -683,8 +694,9 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
     }
     const int srow = sw * 64 + lane;   // scale row this lane loads (A: if < BM)
     const uint8_t* const as_base = gather ? p.a_scales : p.a_scales + (size_t)row0 * kb;
-    as_off = 0;
-    if (FP8 && a_sw && srow < BM) {
+    const uint32_t as_nrec = !kPadZero ? 0xffffffffu : gather ? p.as_bytes : (uint32_t)mrows * (uint32_t)kb;
+    as_off = kPadZero ? as_nrec : 0u;
+    if (FP8 && a_sw && srow < (kPadZero ? mrows : BM)) {
       const int r = min(srow, mrows - 1);
       as_off = (uint32_t)(gather ? p.a_gather[row0 + r] / p.a_gather_div : r) * (uint32_t)kb;
     }
@@ -692,9 +704,9 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
         TILED ? p.w_scales + tile_id * (size_t)(K / 512) * 4096 : p.w_scales + w_expert * (size_t)kb;
     bs_off = TILED ? (uint32_t)(sw * 1024 + lane * 16)
                    : (uint32_t)w_row_of<kSwiGroup>(p.layout, nt, srow, p.N, p.n_out) * (uint32_t)kb;
-    ra = make_rsrc(a_base);
+    ra = make_rsrc(a_base, a_nrec);
     rb = make_rsrc(b_base);
-    ras = make_rsrc(as_base);
+    ras = make_rsrc(as_base, as_nrec);
     rbs = make_rsrc(bs_base);
   };
   // b_step / bs_step: bytes from one stage (one scale group) to the next
@@ -1750,6 +1762,12 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s, int rese
   p.a_scales = a.a_scales;
   p.a_gather = a.a_gather;
   p.a_gather_div = a.a_gather_div;
+  if (a.a_gather) {
+    // (validate_gemm keeps a gathered A below 4 GiB for the DMA kernels)
+    const uint64_t row_bytes = (uint64_t)a.K * (a.a_dtype == MOE_ACT_MXFP8_E4M3 ? 1 : 2);
+    p.a_bytes = (uint32_t)std::min<uint64_t>((uint64_t)a.a_rows * row_bytes, 0xffffffffull);
+    p.as_bytes = (uint32_t)std::min<uint64_t>((uint64_t)a.a_rows * (a.K / 32), 0xffffffffull);
+  }
   p.w = a.w_packed;
   p.w_scales = a.w_scales;
   p.offsets = a.expert_offsets;
