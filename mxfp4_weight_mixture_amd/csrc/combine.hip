@@ -3,8 +3,9 @@
 //   out[t][h] = sum_{j ascending} w[t][j] * y[dest_row[t*k + j]][h]   (fp32)
 // One workgroup per token; each thread owns 8 consecutive h (16-byte bf16
 // or 32-byte fp32 loads), so every row of y is read once, coalesced, and
-// no atomics are involved.  The workgroup is sized to the row (at most 512
-// threads, whole waves, every pass over the row full but the last), and a
+// no atomics are involved.  The workgroup is sized to the row (at most 1024
+// threads for bf16 rows, 512 for fp32 ones, whose 32-byte loads take twice
+// the registers; whole waves, every pass over the row full but the last), and a
 // thread has up to 16 rows of y in flight.  Optionally also writes the next
 // stacked layer's input bf16(out[t] / rms(out[t])).
 #include "internal.h"
@@ -45,21 +46,22 @@ __device__ inline uint32_t bf16_rne(float f) {
 // Rows are fetched kBatch at a time before any is accumulated (more loads in
 // flight per thread); the accumulation order stays j = 0, 1, ..., k-1.
 constexpr int kBatch = 16;
-constexpr int kMaxThreads = 512;   // threads per token, at most
-constexpr int kMaxWaves = kMaxThreads / 64;
+template <typename YT>
+constexpr int max_threads() { return sizeof(YT) == 2 ? 1024 : 512; }   // threads per token, at most
+constexpr int kMaxWaves = 1024 / 64;
 
 // Threads per token for rows of H elements: the fewest passes of at most
-// kMaxThreads threads over the H/8 vectors, then the fewest whole waves that
+// max_threads threads over the H/8 vectors, then the fewest whole waves that
 // cover a pass.
-int combine_threads(int H) {
+int combine_threads(int H, int max_threads) {
   const int nv = H / 8;
-  const int passes = (nv + kMaxThreads - 1) / kMaxThreads;
+  const int passes = (nv + max_threads - 1) / max_threads;
   const int per_pass = (nv + passes - 1) / passes;
   return (per_pass + 63) / 64 * 64;
 }
 
 template <typename YT>
-__global__ __launch_bounds__(kMaxThreads) void combine_kernel(const YT* __restrict__ y,
+__global__ __launch_bounds__(max_threads<YT>()) void combine_kernel(const YT* __restrict__ y,
                                                       const int32_t* __restrict__ dest_row,
                                                       const float* __restrict__ w, int k, int H,
                                                       float* __restrict__ out,
@@ -122,12 +124,11 @@ __global__ __launch_bounds__(kMaxThreads) void combine_kernel(const YT* __restri
 moe_status launch_combine(const void* y, int y_dtype, const int32_t* dest_row, const float* w,
                           int T, int k, int H, float* out, uint16_t* x_next, hipStream_t s) {
   if (T == 0) return MOE_OK;
-  const int threads = combine_threads(H);
   if (y_dtype == MOE_OUT_BF16)
-    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(T), dim3(threads), 0, s,
+    hipLaunchKernelGGL(combine_kernel<uint16_t>, dim3(T), dim3(combine_threads(H, max_threads<uint16_t>())), 0, s,
                        static_cast<const uint16_t*>(y), dest_row, w, k, H, out, x_next);
   else
-    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(threads), 0, s,
+    hipLaunchKernelGGL(combine_kernel<float>, dim3(T), dim3(combine_threads(H, max_threads<float>())), 0, s,
                        static_cast<const float*>(y), dest_row, w, k, H, out, x_next);
   MXMOE_HIP(hipGetLastError());
   return MOE_OK;
