@@ -69,6 +69,13 @@ def parse():
                    help="streamed: move every expert per layer, or only the experts the layer's routing hits")
     p.add_argument("--mfma-rate", action="store_true",
                    help="issue rates of the matrix instructions the GEMM uses (libmxmoe_probe.so), one JSON line")
+    p.add_argument("--phases", action="store_true",
+                   help="where a grouped-GEMM block's time goes, per row-tile class (K loop, the phases between "
+                        "units, small units), for the workload's FC1 and FC2 calls: libmxmoe_phases.so, the same "
+                        "kernels with timers compiled in, one JSON line")
+    p.add_argument("--chunk-stream", action="store_true",
+                   help="rate at which blocks stream contiguous 16 KB chunks, global -> LDS and global -> registers, "
+                        "against blocks and chunks in flight (libmxmoe_probe.so), one JSON line")
     p.add_argument("--traffic-record", default=None, metavar="DIR",
                    help="write profiles/gemm_traffic_<workload>.json from the rocprofv3 counter runs under DIR "
                         "(subfolders pmc_FETCH_SIZE, pmc_WRITE_SIZE, cal_FETCH_SIZE, cal_WRITE_SIZE); no GPU needed")
@@ -854,6 +861,123 @@ def mfma_rates():
     return rec
 
 
+def chunk_stream_rates():
+    """The grouped GEMM's weight-stream access pattern on its own: each block reads its own run of 16 KB
+    chunks (a unit's tiled weight stages), into LDS with the DMA the GEMM uses or into registers, for a few
+    block counts (32 / 64: a few CUs streaming beside idle ones; 256: one block per CU; 448: the decode T=1
+    FC1 shape, 16 experts x 28 n-tiles of 56 stages) and chunks in flight per block."""
+    import ctypes
+    lib = ctypes.CDLL(os.path.join(ROOT, "mxfp4_weight_mixture_amd", "libmxmoe_probe.so"))
+    fn = lib.mxmoe_probe_chunk_stream
+    fn.restype = ctypes.c_float
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.c_int,
+                   ctypes.c_void_p, ctypes.c_void_p]
+    nbytes = 1 << 30
+    buf = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    out = torch.empty(448 * 256, dtype=torch.int32, device="cuda")
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    rec = {"probe": "16 KB chunk stream", "command": "python bench.py --chunk-stream", "runs": []}
+    cases = [(b, ch, 0, d) for b, ch in ((32, 448), (64, 448), (256, 224), (448, 56)) for d in (1, 2, 3, 4, 6, 7)]
+    cases += [(448, 56, 1, d) for d in (1, 2, 4)]
+    for blocks, chunks, mode, depth in cases:
+        fn(buf.data_ptr(), nbytes, blocks, chunks, mode, depth, out.data_ptr(), stream)   # warm-up
+        ms = min(fn(buf.data_ptr(), nbytes, blocks, chunks, mode, depth, out.data_ptr(), stream) for _ in range(3))
+        if ms <= 0:
+            raise RuntimeError("probe launch failed")
+        tot = blocks * chunks * 16384
+        run = {"blocks": blocks, "chunks_per_block": chunks, "path": "global->LDS DMA" if mode == 0 else
+               "global->registers", "chunks_in_flight": depth, "ms": ms, "GBps": tot / (ms * 1e-3) / 1e9,
+               "GBps_per_block": tot / blocks / (ms * 1e-3) / 1e9}
+        rec["runs"].append(run)
+        log(f"[probe] {blocks:3d} blocks, {run['path']:17s}, {depth} x 16 KB in flight: {run['GBps']:6.0f} GB/s "
+            f"({run['GBps_per_block']:5.1f} per block)")
+    del buf, out
+    torch.cuda.empty_cache()
+    return rec
+
+
+PHASE_NAMES = ["k_loop", "barrier_and_draw", "epilogue_to_last_staging_write", "next_setup_first_dma_barrier",
+               "readback_and_stores", "barrier", "rest"]
+
+
+def gemm_phases(args):
+    """Runs the workload's route and permute with libmxmoe.so, then its FC1 and FC2 grouped-GEMM calls with
+    libmxmoe_phases.so (the same kernels with wave 0 of each unit loop reading the 100 MHz s_memrealtime clock
+    at the boundaries of a unit's phases; the timers change the kernels' register allocation, so their times
+    are a close, not an exact, image of the library's).  Per call and row-tile class: units, mean time per
+    unit of each phase, the blocks' summed time, and the spread of the loops' starts and ends."""
+    import ctypes
+    ph = ctypes.CDLL(os.path.join(ROOT, "mxfp4_weight_mixture_amd", "libmxmoe_phases.so"))
+    ph.moe_mxfp4_grouped_gemm.restype = ctypes.c_int
+    ph.moe_mxfp4_grouped_gemm.argtypes = [ctypes.POINTER(mx.GemmArgs), ctypes.c_void_p, ctypes.c_size_t,
+                                          ctypes.c_void_p]
+    name = args.workload
+    shape = gen.preset(name, **({"T": args.tokens} if args.tokens else {}))
+    li = gen.layer_inputs(shape) if shape.act != "mxfp8" else gen.LayerInputs(
+        shape, gen.activations_bf16(shape), gen.router_logits(shape))
+    x_bf16 = li.x_bf16.to("cuda")
+    x, xs = gen.quantize_mxfp8(x_bf16.float()) if shape.act == "mxfp8" else (x_bf16, None)
+    logits = torch.from_numpy(li.logits).to("cuda")
+    w = gen.all_expert_weights(shape, 0, "cuda")
+    inter = args.inter or ("mxfp8" if shape.act == "mxfp8" and shape.H % 512 == 0 else "bf16")
+    w_format = args.w_format or ("tiled" if shape.H % 512 == 0 and shape.I % 512 == 0 else "canonical")
+    if w_format == "tiled":
+        t1 = mx.tile_weights(w[0], w[1], shape.layout)
+        t2 = mx.tile_weights(w[2], w[3], "none")
+        w = (*t1, *t2)
+        del t1, t2
+        torch.cuda.empty_cache()
+    steps = Steps(shape, w, x, xs, logits, inter, w_format)
+    for _ in range(3):
+        steps.run()
+    torch.cuda.synchronize()
+    stream = ctypes.c_void_p(torch.cuda.current_stream().cuda_stream)
+    buf = np.zeros(2048 * 4 * 12, dtype=np.uint64)
+    rec = {"probe": "grouped-GEMM phase timers", "workload": name, "T": shape.T, "inter": inter,
+           "command": f"python bench.py --phases --workload {name}" + (f" --tokens {args.tokens}" if args.tokens else ""),
+           "calls": {}}
+    for which, g in (("fc1", steps.g1), ("fc2", steps.g2)):
+        for _ in range(3):
+            mx._check(ph.moe_mxfp4_grouped_gemm(ctypes.byref(g), ctypes.c_void_p(steps.gws.data_ptr()), steps.gws_n, stream))
+        torch.cuda.synchronize()
+        if ph.mxmoe_phase_timers_reset() != 0:
+            raise RuntimeError("phase timer reset failed")
+        ev = [torch.cuda.Event(enable_timing=True) for _ in range(2)]
+        ev[0].record()
+        mx._check(ph.moe_mxfp4_grouped_gemm(ctypes.byref(g), ctypes.c_void_p(steps.gws.data_ptr()), steps.gws_n, stream))
+        ev[1].record()
+        torch.cuda.synchronize()
+        if ph.mxmoe_phase_timers_read(ctypes.c_void_p(buf.ctypes.data)) != 0:
+            raise RuntimeError("phase timer read failed")
+        d = buf.reshape(2048, 4, 12)
+        call = {"call_ms": ev[0].elapsed_time(ev[1]), "classes": {}}
+        starts = [int(~np.uint64(v)) for v in d[:, :, 10].max(axis=1) if v]
+        ends = [int(v) for v in d[:, :, 11].max(axis=1) if v]
+        if starts:
+            t0 = min(starts)
+            call["loop_start_spread_us"] = (max(starts) - t0) * 10 / 1e3
+            call["first_loop_end_us"] = (min(ends) - t0) * 10 / 1e3
+            call["last_loop_end_us"] = (max(ends) - t0) * 10 / 1e3
+        for ci, bm in enumerate((32, 64, 128, 256)):
+            n = int(d[:, ci, 7].sum())
+            if n == 0:
+                continue
+            per = {PHASE_NAMES[j]: float(d[:, ci, j].sum()) * 10 / 1e3 / n for j in range(7)}
+            runs = int(d[:, ci, 9].sum())
+            call["classes"][f"{bm}_rows"] = {
+                "units": n, "us_per_unit": per,
+                "block_ms": float(d[:, ci, :7].sum()) * 10 / 1e6,
+                "first_setup_us": float(d[:, ci, 8].sum()) * 10 / 1e3 / max(runs, 1), "loops": runs}
+            log(f"[phases] {which} {bm:3d}-row units {n:6d}: " +
+                ", ".join(f"{k} {v:.2f}" for k, v in per.items()) + f" us; block-ms {call['classes'][f'{bm}_rows']['block_ms']:.1f}")
+        rec["calls"][which] = call
+        log(f"[phases] {which}: call {call['call_ms']:.3f} ms, loops start within "
+            f"{call.get('loop_start_spread_us', 0):.1f} us, end {call.get('first_loop_end_us', 0):.1f}-"
+            f"{call.get('last_loop_end_us', 0):.1f} us after the first start")
+    return rec
+
+
 def main():
     args = parse()
     if args.traffic_record:
@@ -869,6 +993,15 @@ def main():
 
     if args.mfma_rate:
         print(json.dumps(mfma_rates()))
+        return
+    if args.chunk_stream:
+        print(json.dumps(chunk_stream_rates()))
+        return
+    if args.phases:
+        if args.workload == "streamed":
+            print("--phases times a resident layer's GEMM calls, not the streamed pass", file=sys.stderr)
+            sys.exit(2)
+        print(json.dumps(gemm_phases(args)))
         return
     if args.copy_calibration:
         n = 1 << 30

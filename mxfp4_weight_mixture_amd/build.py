@@ -6,6 +6,11 @@ Every .hip file under csrc/ is compiled for gfx950 only, in parallel, then
 linked into mxfp4_weight_mixture_amd/libmxmoe.so.  Packed-FP32 VALU ops are
 disabled for the device code (-packed-fp32-ops): the compiler would otherwise
 form v_pk_* fp32 instructions from ordinary float code.
+
+Two measurement libraries are built beside it: libmxmoe_probe.so (probe/:
+matrix-instruction issue rates, HBM stream read, 16 KB chunk streams) and
+libmxmoe_phases.so, the same sources with the grouped GEMM's phase timers
+compiled in (MXMOE_PHASE_TIMERS=1), which `bench.py --phases` loads.
 """
 from __future__ import annotations
 
@@ -24,6 +29,7 @@ LIB = os.path.join(PKG, "libmxmoe.so")
 # outside libmxmoe's ABI
 PROBE_DIR = os.path.join(PKG, "probe")
 PROBE_LIB = os.path.join(PKG, "libmxmoe_probe.so")
+PHASES_LIB = os.path.join(PKG, "libmxmoe_phases.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 ARCH = "gfx950"
@@ -42,9 +48,9 @@ def hipcc() -> str:
     raise RuntimeError("hipcc not found (ROCm is required to build libmxmoe.so)")
 
 
-def _compile(src: str) -> str:
-    obj = os.path.join(BUILD_DIR, os.path.basename(src) + ".o")
-    cmd = [hipcc(), *CXXFLAGS, "-c", src, "-o", obj]
+def _compile(src: str, phases: bool = False) -> str:
+    obj = os.path.join(BUILD_DIR, os.path.basename(src) + (".phases.o" if phases else ".o"))
+    cmd = [hipcc(), *CXXFLAGS, *(["-DMXMOE_PHASE_TIMERS=1"] if phases else []), "-c", src, "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     if r.returncode != 0:
         raise RuntimeError(f"compiling {src} failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
@@ -56,14 +62,23 @@ def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
     srcs = sorted(glob.glob(os.path.join(CSRC, "*.hip")))
     jobs = min(len(srcs), max(1, min(16, os.cpu_count() or 1)))
-    with cf.ThreadPoolExecutor(jobs) as ex:
+    gemm = os.path.join(CSRC, "gemm.hip")
+    with cf.ThreadPoolExecutor(jobs + 1) as ex:
+        phases_obj = ex.submit(_compile, gemm, True)
         objs = list(ex.map(_compile, srcs))
-    tmp = LIB + ".tmp"
-    cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *objs, "-o", tmp]
-    r = subprocess.run(cmd, capture_output=True, text=True)
-    if r.returncode != 0:
-        raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
-    os.replace(tmp, LIB)
+        phases_obj = phases_obj.result()
+
+    def link(lib, lib_objs):
+        tmp = lib + ".tmp"
+        cmd = [hipcc(), "-shared", "-fPIC", f"--offload-arch={ARCH}", *lib_objs, "-o", tmp]
+        r = subprocess.run(cmd, capture_output=True, text=True)
+        if r.returncode != 0:
+            raise RuntimeError(f"linking failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
+        os.replace(tmp, lib)
+
+    link(LIB, objs)
+    gemm_obj = os.path.join(BUILD_DIR, "gemm.hip.o")
+    link(PHASES_LIB, [o for o in objs if o != gemm_obj] + [phases_obj])
     tmp = PROBE_LIB + ".tmp"
     cmd = [hipcc(), *CXXFLAGS, "-shared", *sorted(glob.glob(os.path.join(PROBE_DIR, "*.hip"))), "-o", tmp]
     r = subprocess.run(cmd, capture_output=True, text=True)
@@ -71,7 +86,7 @@ def build(verbose: bool = False) -> str:
         raise RuntimeError(f"building the probe failed:\n{' '.join(cmd)}\n{r.stdout}\n{r.stderr}")
     os.replace(tmp, PROBE_LIB)
     if verbose:
-        print("built", LIB, "and", PROBE_LIB)
+        print("built", LIB, "and the measurement libraries", PROBE_LIB, PHASES_LIB)
     return LIB
 
 

@@ -63,6 +63,60 @@ constexpr int kAStride = 144;     // bytes per LDS A row (128 + 16 pad)
 constexpr int kClasses = 4;       // row-tile sizes 32, 64, 128, 256
 constexpr int kXcds = 8;
 
+// Phase timers: measurement tooling, compiled in only with
+// MXMOE_PHASE_TIMERS=1 (libmxmoe_phases.so; the library proper has none).
+// Wave 0 of each unit loop reads the 100 MHz s_memrealtime clock at the
+// boundaries of a unit's phases and adds the durations, per block and
+// row-tile class, into g_phase: [0] the K loop (from the issue of its first
+// stages to its last product), between two units [1] the barrier and the
+// next unit's draw, [2] the epilogue up to the last staging write, [3] the
+// next unit's set-up, its first DMA and a barrier, [4] the staging's
+// read-back and stores, [5] a barrier, [6] the rest (the next unit's other
+// stages; a direct epilogue's whole time); [7] units, [8] the first unit's
+// set-up, [9] unit loops run, [10] the complement of the earliest loop
+// start, [11] the latest loop end (raw clock values: max over the block).
+#ifndef MXMOE_PHASE_TIMERS
+#define MXMOE_PHASE_TIMERS 0
+#endif
+constexpr int kPhaseSlots = 12;
+#if MXMOE_PHASE_TIMERS
+constexpr int kPhaseBlocks = 2048;
+__device__ unsigned long long g_phase[kPhaseBlocks][kClasses][kPhaseSlots];
+#endif
+
+struct PhaseClock {
+#if MXMOE_PHASE_TIMERS
+  unsigned long long entry, last, d[7] = {0, 0, 0, 0, 0, 0, 0}, units = 0, setup = 0;
+  __device__ PhaseClock() { entry = last = __builtin_amdgcn_s_memrealtime(); }
+  // the first unit's stages are issued: its K loop starts
+  __device__ void loop_start() {
+    last = __builtin_amdgcn_s_memrealtime();
+    setup = last - entry;
+  }
+  // phase i ends now
+  __device__ void lap(int i) {
+    const unsigned long long t = __builtin_amdgcn_s_memrealtime();
+    d[i] += t - last;
+    last = t;
+    if (i == 0) ++units;
+  }
+  __device__ void flush(int cls, bool record) {
+    if (!record || blockIdx.x >= kPhaseBlocks) return;
+    unsigned long long* g = g_phase[blockIdx.x][cls];
+    for (int i = 0; i < 7; ++i) atomicAdd(g + i, d[i]);
+    atomicAdd(g + 7, units);
+    atomicAdd(g + 8, setup);
+    atomicAdd(g + 9, 1ull);
+    atomicMax(g + 10, ~entry);
+    atomicMax(g + 11, (unsigned long long)__builtin_amdgcn_s_memrealtime());
+  }
+#else
+  __device__ void loop_start() {}
+  __device__ void lap(int) {}
+  __device__ void flush(int, bool) {}
+#endif
+};
+
 struct Tile {
   int expert;
   int row0;
@@ -740,11 +794,13 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
     if (b_sw) dma16(rbs, bs_off, bs_step * j, base + C::SG_A + sw * 1024);
   };
 
+  PhaseClock clock;
   setup(__builtin_amdgcn_readfirstlane(u));
   issue_scales(0);
   issue(0);
   issue(1);
   issue(2);
+  clock.loop_start();
   for (;;) {
     const int lane = lane_id();
     const int wave = wave_u;
@@ -1041,9 +1097,11 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
 
 
     // ---- between units ----
+    clock.lap(0);
     stage_barrier();   // every wave is done reading the stage and scale buffers
     const int e_row0 = row0, e_mrows = mrows, e_nt = nt;
     const int un = __builtin_amdgcn_readfirstlane(next());
+    clock.lap(1);
     // the next unit's set-up and first PF stages: issued once the accumulators
     // are dead (after the last staging write; before a direct epilogue), so that
     // its offsets need no registers beside them
@@ -1185,8 +1243,12 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
               }
             }
           }
-          if (pass == EC::PASSES - 1) prefetch();
+          if (pass == EC::PASSES - 1) {
+            clock.lap(2);
+            prefetch();
+          }
           stage_barrier();
+          if (pass == EC::PASSES - 1) clock.lap(3);
           // The pass's rows -> C in whole row segments, 16 bytes a thread.  The
           // staging is read with lds_read16/lds_read4 (see there): a plain LDS
           // read here would be ordered after the next unit's DMA just issued.
@@ -1240,12 +1302,17 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
               }
             }
           }
+          if (pass == EC::PASSES - 1) clock.lap(4);
           stage_barrier();   // the staging is read before anything writes it again
+          if (pass == EC::PASSES - 1) clock.lap(5);
         }
       }
     }
     settle();
-    if (un < 0) break;
+    if (un < 0) {
+      clock.lap(6);
+      break;
+    }
     if constexpr (!EC::EARLY) {
       setup(un);
       issue_scales(0);
@@ -1254,7 +1321,9 @@ __device__ __forceinline__ void run_units(const Params& p, int u, int count, int
     // without the early start)
 #pragma unroll
     for (int s = EC::EARLY ? EC::PF : 0; s < C::NST; ++s) issue(s);
+    clock.lap(6);
   }
+  clock.flush(BM == 32 ? 0 : BM == 64 ? 1 : BM == 128 ? 2 : 3, tid_in == 0 && store);
 }
 
 template <int BM, bool FP8, int EPI, int OUT, bool TILED>
@@ -1304,9 +1373,9 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
 // (the remainders of experts with few rows: the tail of a skewed routing)
 // only stream their experts' weights, and the 64- and 128-row tiles sit in
 // between.  Run one class after another, the weight stream runs with the
-// matrix cores idle, and a <= 32-row block streams at most about 35 GB/s
-// however few blocks run beside it (latency-bound per block), so that stream
-// needs many CUs at once.  Here every CU runs one block of eight waves that
+// matrix cores idle; and one block streams at most some tens of GB/s (its
+// three-stage ring keeps two stages in flight: about 27 GB/s per <= 32-row
+// unit beside the full tiles), so that stream needs many CUs at once.  Here every CU runs one block of eight waves that
 // works through the classes' unit queues in turn: kSmallCus blocks per XCD
 // take the <= 32-row units first (two at a time: waves 0-3 and 4-7 each run
 // one unit in their own half of the LDS), then the 64-, 128- and 256-row
@@ -1796,3 +1865,20 @@ moe_status launch_gemm(const moe_gemm_args& a, void* ws, hipStream_t s, int rese
 }
 
 }  // namespace mxmoe
+
+#if MXMOE_PHASE_TIMERS
+extern "C" {
+
+// Phase timers (libmxmoe_phases.so only): zero them / copy them to host
+// memory (unsigned long long [2048][4][12], layout as g_phase).  0 on success.
+int mxmoe_phase_timers_reset() {
+  static unsigned long long zero[mxmoe::kPhaseBlocks * mxmoe::kClasses * mxmoe::kPhaseSlots];
+  return hipMemcpyToSymbol(HIP_SYMBOL(mxmoe::g_phase), zero, sizeof(zero)) == hipSuccess ? 0 : 1;
+}
+int mxmoe_phase_timers_read(void* host) {
+  if (!host) return 1;
+  return hipMemcpyFromSymbol(host, HIP_SYMBOL(mxmoe::g_phase), sizeof(mxmoe::g_phase)) == hipSuccess ? 0 : 1;
+}
+
+}  // extern "C"
+#endif
