@@ -1397,8 +1397,9 @@ __global__ __launch_bounds__(512) void gemm_mixed_kernel(Params p, int small_cus
   constexpr int kSlots = CF::NST * CF::LDS_STAGE + CF::LDS_SG;   // scale buffer 1 of the 256-row units
   static_assert(kSmallHalfLds + CS::LDS_TOTAL <= kSlots && Cfg2<128, FP8, 8>::LDS_TOTAL <= kSlots,
                 "the draw slots lie beyond the LDS of every unit but the 256-row ones");
+  static_assert(kSlots + 3 * sizeof(int) <= CF::LDS_TOTAL, "three slots inside the LDS");
   __shared__ __attribute__((aligned(1024))) uint8_t lds[CF::LDS_TOTAL];
-  int* const slot = reinterpret_cast<int*>(lds + kSlots);   // this block's next draw, per half
+  int* const slot = reinterpret_cast<int*>(lds + kSlots);   // this block's next draw, per half; [2]: the end game's queues
 
   const int xcd = blockIdx.x % kXcds;
   const bool small_first = blockIdx.x / kXcds < small_cus;
@@ -1408,67 +1409,97 @@ __global__ __launch_bounds__(512) void gemm_mixed_kernel(Params p, int small_cus
   int32_t* const ctr = p.unit_ctr;
   auto none = []() -> int { return -1; };
 
-  int ph = 0;          // position in this block's queue order
-  bool have = false;   // <= 32-row queue: the slots already hold the next draws
-  while (ph < kClasses) {
-    const int c = small_first ? ph : kClasses - 1 - ph;   // row-tile class of the current queue
-    const int cnt = counts[c];
-    const int units = cnt * p.n_tiles;
-    const int per_xcd = (units + kXcds - 1) / kXcds;
-    const int u0 = xcd * per_xcd, u1 = min(units, u0 + per_xcd);
-    int32_t* const uc = ctr + c * kXcds + xcd;
-    Params q = p;
-    q.tiles = lists + c * p.tile_cap;
-    if (c == 0) {
-      // two units side by side, one per half, each drawn by the half's first thread
-      const bool drawer = (threadIdx.x & 255) == 0;
-      if (!have && drawer) slot[half] = atomicAdd(uc, 1);
+  // The block drains its own XCD's queues first, then (the end game) those of
+  // the other XCDs in turn: the XCDs do not finish their ranges together
+  // (prefill896 FC1: their last blocks ended up to 0.36 ms apart), and a
+  // block whose XCD is done adds its matrix cores to a late XCD's work.  For
+  // the end game thread 0 reads every queue's counter once and the block
+  // visits only the queues that still held units then (a counter only grows,
+  // so a stale read can only add a visit that draws nothing).
+  uint32_t open = 0;   // bit c * kXcds + x: queue (class c, XCD x) had units left
+  for (int k = 0; k < kXcds; ++k) {
+    const int x = (xcd + k) % kXcds;   // the XCD whose queues this round drains
+    if (k == 1) {
+      if (threadIdx.x == 0) {
+        uint32_t m = 0;
+        for (int c = 0; c < kClasses; ++c) {
+          const int units = counts[c] * p.n_tiles;
+          const int per_xcd = (units + kXcds - 1) / kXcds;
+          for (int y = 0; y < kXcds; ++y)
+            if (ctr[c * kXcds + y] < min(units, (y + 1) * per_xcd) - y * per_xcd) m |= 1u << (c * kXcds + y);
+        }
+        slot[2] = (int)m;
+      }
       stage_barrier();
-      const int a = u0 + slot[0], b = u0 + slot[1];
-      stage_barrier();   // both slots read before either is written again
-      const bool va = a < u1, vb = b < u1;
-      if (!va && !vb) {
+      open = (uint32_t)__builtin_amdgcn_readfirstlane(slot[2]);
+      stage_barrier();   // read before any unit's LDS use
+    }
+    int ph = 0;          // position in this block's queue order
+    bool have = false;   // <= 32-row queue: the slots already hold the next draws
+    while (ph < kClasses) {
+      const int c = small_first ? ph : kClasses - 1 - ph;   // row-tile class of the current queue
+      if (k > 0 && !((open >> (c * kXcds + x)) & 1u)) {
         ++ph;
-        have = false;
         continue;
       }
-      int nxt = 0;
-      if (drawer) nxt = atomicAdd(uc, 1);   // one unit ahead
-      const bool mine = half ? vb : va;
-      const int u = (half ? vb : !va) ? b : a;   // a half without a unit runs its partner's
-      run_units<32, FP8, EPI, OUT, true, 4>(q, u, cnt, threadIdx.x & 255, lds + half * kSmallHalfLds, mine, none,
-                                            [] {});
-      stage_barrier();   // every wave is done with the LDS
-      if (drawer) slot[half] = nxt;
-      have = true;
-      continue;
-    }
-    // one unit stream for the whole block, the next unit's first stages under each epilogue
-    if (threadIdx.x == 0) slot[0] = atomicAdd(uc, 1);
-    stage_barrier();
-    const int a = u0 + slot[0];
-    stage_barrier();   // the slot is read before it is written again
-    if (a < u1) {
-      // thread 0's draws, one unit ahead, as in gemm_dma_kernel
-      int d = 0;
-      if (threadIdx.x == 0) d = atomicAdd(uc, 1);
-      int drawn = __builtin_amdgcn_readfirstlane(d);
-      auto next = [&]() -> int {
-        if (threadIdx.x == 0) slot[0] = drawn;
+      const int cnt = counts[c];
+      const int units = cnt * p.n_tiles;
+      const int per_xcd = (units + kXcds - 1) / kXcds;
+      const int u0 = x * per_xcd, u1 = min(units, u0 + per_xcd);
+      int32_t* const uc = ctr + c * kXcds + x;
+      Params q = p;
+      q.tiles = lists + c * p.tile_cap;
+      if (c == 0) {
+        // two units side by side, one per half, each drawn by the half's first thread
+        const bool drawer = (threadIdx.x & 255) == 0;
+        if (!have && drawer) slot[half] = atomicAdd(uc, 1);
         stage_barrier();
-        const int n = u0 + slot[0];
-        d = 0;
-        if (threadIdx.x == 0 && n < u1) d = atomicAdd(uc, 1);
-        return n < u1 ? n : -1;
-      };
-      auto settle = [&]() { drawn = __builtin_amdgcn_readfirstlane(d); };
-      if (c == 3) run_units<256, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true, next, settle);
-      else if (c == 2) run_units<128, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true, next, settle);
-      else run_units<64, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true, next, settle);
-      stage_barrier();   // every wave is done with the LDS and the slot
+        const int a = u0 + slot[0], b = u0 + slot[1];
+        stage_barrier();   // both slots read before either is written again
+        const bool va = a < u1, vb = b < u1;
+        if (!va && !vb) {
+          ++ph;
+          have = false;
+          continue;
+        }
+        int nxt = 0;
+        if (drawer) nxt = atomicAdd(uc, 1);   // one unit ahead
+        const bool mine = half ? vb : va;
+        const int u = (half ? vb : !va) ? b : a;   // a half without a unit runs its partner's
+        run_units<32, FP8, EPI, OUT, true, 4>(q, u, cnt, threadIdx.x & 255, lds + half * kSmallHalfLds, mine, none,
+                                              [] {});
+        stage_barrier();   // every wave is done with the LDS
+        if (drawer) slot[half] = nxt;
+        have = true;
+        continue;
+      }
+      // one unit stream for the whole block, the next unit's first stages under each epilogue
+      if (threadIdx.x == 0) slot[0] = atomicAdd(uc, 1);
+      stage_barrier();
+      const int a = u0 + slot[0];
+      stage_barrier();   // the slot is read before it is written again
+      if (a < u1) {
+        // thread 0's draws, one unit ahead, as in gemm_dma_kernel
+        int d = 0;
+        if (threadIdx.x == 0) d = atomicAdd(uc, 1);
+        int drawn = __builtin_amdgcn_readfirstlane(d);
+        auto next = [&]() -> int {
+          if (threadIdx.x == 0) slot[0] = drawn;
+          stage_barrier();
+          const int n = u0 + slot[0];
+          d = 0;
+          if (threadIdx.x == 0 && n < u1) d = atomicAdd(uc, 1);
+          return n < u1 ? n : -1;
+        };
+        auto settle = [&]() { drawn = __builtin_amdgcn_readfirstlane(d); };
+        if (c == 3) run_units<256, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true, next, settle);
+        else if (c == 2) run_units<128, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true, next, settle);
+        else run_units<64, FP8, EPI, OUT, true, 8>(q, a, cnt, threadIdx.x, lds, true, next, settle);
+        stage_barrier();   // every wave is done with the LDS and the slot
+      }
+      have = false;
+      ++ph;
     }
-    have = false;
-    ++ph;
   }
 }
 
