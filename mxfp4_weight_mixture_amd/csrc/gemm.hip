@@ -1335,36 +1335,60 @@ __global__ __launch_bounds__((64 * dma_waves<BM, FP8, EPI>())) void gemm_dma_ker
   const int units = count * p.n_tiles;
   const int xcd = blockIdx.x % kXcds;
   const int per_xcd = (units + kXcds - 1) / kXcds;
-  const int u_first = xcd * per_xcd;
-  const int u_end = min(units, u_first + per_xcd);
 
   // Units of an XCD's range are handed out dynamically (blocks whose units
   // end early take more; blocks that start late take fewer).  Thread 0 draws
   // the next index with an atomic one unit ahead; the index reaches the other
   // threads through a slot in scale buffer 1, which is idle between a unit's
-  // last products and the next unit's second stage.
-  int* const unit_slot = reinterpret_cast<int*>(lds + C::NST * C::LDS_STAGE + C::LDS_SG);
-  if (threadIdx.x == 0) *unit_slot = atomicAdd(&p.unit_ctr[xcd], 1);
-  stage_barrier();
-  const int u = u_first + *unit_slot;
-  if (u >= u_end) return;   // the same in every thread
-  // Thread 0's draw of the unit after the current one, in a scalar register
-  // (wave 0's first lane is thread 0).  next() publishes it and issues the
-  // following draw; settle() takes that draw's result after the epilogue, so
-  // that the atomic's latency passes under it.
-  int d = 0;
-  if (threadIdx.x == 0) d = atomicAdd(&p.unit_ctr[xcd], 1);
-  int drawn = __builtin_amdgcn_readfirstlane(d);
-  auto next = [&]() -> int {
-    if (threadIdx.x == 0) *unit_slot = drawn;
+  // last products and the next unit's second stage.  A block drains its own
+  // XCD's range first, then (the end game) the other XCDs' ranges that still
+  // held units when thread 0 read their counters after its own range (a
+  // counter only grows: a stale read can only add a visit that draws nothing).
+  // With fewer than two units per block (decode at T <= 2) every range is
+  // drawn out by the blocks' first draws, and the end game is skipped.
+  int* const slot = reinterpret_cast<int*>(lds + C::NST * C::LDS_STAGE + C::LDS_SG);
+  const int rounds = units >= 2 * (int)gridDim.x ? kXcds : 1;
+  uint32_t open = 0;   // bit x: XCD x's range had units left
+  for (int k = 0; k < rounds; ++k) {
+    const int x = (xcd + k) % kXcds;   // the XCD whose range this round drains
+    if (k == 1) {
+      if (threadIdx.x == 0) {
+        uint32_t m = 0;
+        for (int y = 0; y < kXcds; ++y)
+          if (p.unit_ctr[y] < min(units, (y + 1) * per_xcd) - y * per_xcd) m |= 1u << y;
+        slot[1] = (int)m;
+      }
+      stage_barrier();
+      open = (uint32_t)__builtin_amdgcn_readfirstlane(slot[1]);
+      stage_barrier();   // read before any unit's LDS use
+    }
+    if (k > 0 && !((open >> x) & 1u)) continue;
+    const int u_first = x * per_xcd;
+    const int u_end = min(units, u_first + per_xcd);
+    if (threadIdx.x == 0) slot[0] = atomicAdd(&p.unit_ctr[x], 1);
     stage_barrier();
-    const int n = u_first + *unit_slot;
-    d = 0;
-    if (threadIdx.x == 0 && n < u_end) d = atomicAdd(&p.unit_ctr[xcd], 1);
-    return n < u_end ? n : -1;
-  };
-  auto settle = [&]() { drawn = __builtin_amdgcn_readfirstlane(d); };
-  run_units<BM, FP8, EPI, OUT, TILED, C::NW>(p, u, count, threadIdx.x, lds, true, next, settle);
+    const int u = u_first + slot[0];
+    stage_barrier();   // the slot is read before it is written again
+    if (u >= u_end) continue;   // the same in every thread
+    // Thread 0's draw of the unit after the current one, in a scalar register
+    // (wave 0's first lane is thread 0).  next() publishes it and issues the
+    // following draw; settle() takes that draw's result after the epilogue, so
+    // that the atomic's latency passes under it.
+    int d = 0;
+    if (threadIdx.x == 0) d = atomicAdd(&p.unit_ctr[x], 1);
+    int drawn = __builtin_amdgcn_readfirstlane(d);
+    auto next = [&]() -> int {
+      if (threadIdx.x == 0) slot[0] = drawn;
+      stage_barrier();
+      const int n = u_first + slot[0];
+      d = 0;
+      if (threadIdx.x == 0 && n < u_end) d = atomicAdd(&p.unit_ctr[x], 1);
+      return n < u_end ? n : -1;
+    };
+    auto settle = [&]() { drawn = __builtin_amdgcn_readfirstlane(d); };
+    run_units<BM, FP8, EPI, OUT, TILED, C::NW>(p, u, count, threadIdx.x, lds, true, next, settle);
+    stage_barrier();   // every wave is done with the LDS and the slots
+  }
 }
 
 // ---- every row-tile class of a call in one launch ------------------------
