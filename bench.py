@@ -827,6 +827,12 @@ def bench_streamed(args):
         "roofline": {"bound": "h2d", "achieved": achieved, "peak": h2d_peak, "unit": "GB/s",
                      "frac": achieved / h2d_peak, "traffic": None, "kernel": "host->device weight stream"},
     }
+    if args.expert_copy != "all":
+        rec["routed_copy_note"] = (
+            "the copy stream routes each layer from that layer's router logits before the previous layer's "
+            "compute ends, which works because this call receives every layer's logits up front; in a stacked "
+            "model a layer's router input is the previous layer's output, so there the hit set is known only "
+            "after that layer, and the pass without routing (all_experts_ms) is the one that applies")
     return rec
 
 
