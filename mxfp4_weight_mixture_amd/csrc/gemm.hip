@@ -16,20 +16,26 @@
 //     (the MXFP8 x MXFP4 product of the Kimi-K3 page, goal section).
 //
 // Work decomposition.  A small planning kernel splits each expert's rows
-// into 256-row tiles plus one remainder tile, and files every tile under
-// one of four row-tile sizes (32, 64, 128, 256) so that an expert with a
-// handful of rows (the decode shapes, the tail of a skewed routing) does
-// not pay for 256 rows of matrix-core work.  One persistent launch per tile
-// size walks its list; a (tile, n-tile) unit is one 256-column slice of one
-// row tile.  Units are dealt to the 8 XCDs in contiguous ranges, n-tile
-// fastest, so that the blocks sharing an XCD's L2 work on the same rows.
+// into full tiles (256 rows; 128 with bf16 activations) plus one remainder
+// tile, and files every tile under one of four row-tile sizes (32, 64, 128,
+// 256) so that an expert with a handful of rows (the decode shapes, the tail
+// of a skewed routing) does not pay for 256 rows of matrix-core work.  A
+// (tile, n-tile) unit is one 256-column slice of one row tile.  Units are
+// dealt to the 8 XCDs in contiguous ranges (in groups of row tiles x all
+// n-tiles, row tile fastest), so that the blocks sharing an XCD's L2 share A
+// rows and weight tiles; inside a range blocks draw units with an atomic,
+// and a block whose XCD is done takes the other XCDs' remaining units.  With
+// MXFP8 activations and a 256-row class, one persistent launch runs every
+// class (gemm_mixed_kernel: the <= 32-row units' weight stream under the
+// full tiles' matrix-core work); otherwise one persistent launch per class
+// (gemm_dma_kernel).
 //
-// Block: 256 threads = 4 wave64s.  Per K stage (128 bytes of each A row:
-// 128 FP8 or 64 bf16 elements) the A tile, the B tile and their scales go
-// global -> registers -> LDS (double-buffered, one barrier per stage); the
-// global loads for stage s+1 are in flight while stage s is multiplied.
-// LDS rows are padded by 16 bytes so that the 16-byte fragment reads of 8
-// consecutive rows land on distinct banks.
+// K loop (K % 512 == 0): per 128-element K stage the A rows (gathered
+// through the permutation), the weight rows and, every four stages, both
+// scales' 16-byte groups go global -> LDS with buffer_load ... lds into a
+// ring of three stage buffers, two stages ahead of the products, the LDS
+// layout swizzled so that fragment reads are conflict-free.  Other K use the
+// register-staged gemm_kernel (global -> registers -> padded LDS).
 //
 // MFMA operand layout used (32x32 tiles, measured on gfx950 with one-hot
 // operands): lane l supplies row/column (l % 32).  For the scaled
